@@ -1,0 +1,452 @@
+// C ABI of the scoring library: argument validation, workspace layout,
+// launch sequencing on the caller's stream, status mapping and optional
+// per-kernel event timing.  Every check runs on the host before anything is
+// enqueued, and no HIP call is made on an invalid argument.
+#include "../../include/speckv.h"
+#include "kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+using namespace skv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Dims {
+  int64_t L, Hq, Hkv, D, n_in, stride, n_window, n_lookahead, esize;
+  float scale;
+  int dtype;
+};
+
+skv_status check_shape(const skv_shape* s, Dims* d) {
+  if (!s) return SKV_ERR_NULL;
+  if (s->dtype != SKV_F32 && s->dtype != SKV_BF16) return SKV_ERR_DTYPE;
+  if (s->n_layers < 1 || s->n_kv_heads < 1 || s->n_q_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+    return SKV_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return SKV_ERR_SHAPE;
+  if (s->n_in < 1 || s->n_in > INT32_MAX - 1024) return SKV_ERR_SHAPE;
+  if (s->n_window < 0 || s->n_lookahead < 0 || s->n_window > s->n_in) return SKV_ERR_SHAPE;
+  if (!(s->scale >= 0.f) || std::isinf(s->scale)) return SKV_ERR_PARAM;
+  d->L = s->n_layers;
+  d->Hq = s->n_q_heads;
+  d->Hkv = s->n_kv_heads;
+  d->D = s->head_dim;
+  d->n_in = s->n_in;
+  d->esize = (s->dtype == SKV_F32) ? 4 : 2;
+  d->stride = s->kv_head_stride ? s->kv_head_stride : s->n_in * s->head_dim;
+  if (d->stride < d->n_in * d->D) return SKV_ERR_SHAPE;
+  if ((d->stride * d->esize) % 16 != 0) return SKV_ERR_ALIGN;
+  d->n_window = s->n_window;
+  d->n_lookahead = s->n_lookahead;
+  d->scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->head_dim));
+  d->dtype = s->dtype;
+  const int64_t G = d->Hq / d->Hkv;
+  // row counts and unit counts must stay inside int32 for the kernels
+  if (G * (d->n_window + d->n_lookahead) > INT32_MAX / 2 || d->L * d->Hkv > INT32_MAX / 2) return SKV_ERR_SHAPE;
+  return SKV_OK;
+}
+
+// ---- workspace layouts -------------------------------------------------
+struct ScoreWs {
+  size_t part, lam, end;
+};
+ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
+  const int64_t kpb = score_keys_per_block(d.dtype, (int)d.D);
+  const int64_t chunks = (keys + kpb - 1) / kpb;
+  ScoreWs w;
+  w.part = 0;
+  w.lam = round_up((size_t)(units * chunks * rows) * sizeof(float2));
+  w.end = w.lam + round_up((size_t)(units * rows) * sizeof(float));
+  return w;
+}
+
+struct PcWs {
+  ScoreWs sc;
+  size_t rowmax, end;
+};
+PcWs specpc_ws(const Dims& d, int64_t units) {
+  const int64_t G = d.Hq / d.Hkv, W = d.n_window;
+  PcWs w;
+  w.sc = score_ws(d, units, G * W, d.n_in);
+  const int64_t rpb = specpc_rows_per_block(d.dtype, (int)d.D);
+  const int64_t nrb = (W + rpb - 1) / rpb;
+  w.rowmax = w.sc.end;
+  w.end = w.rowmax + round_up((size_t)(nrb * d.n_in) * sizeof(float));
+  return w;
+}
+
+int64_t keep_count(const Dims& d, int64_t C_max) {
+  const int64_t n_pre = d.n_in - d.n_window;
+  return (C_max < n_pre ? C_max : n_pre) + d.n_window;
+}
+
+// ---- optional event profiling -----------------------------------------
+struct ProfEntry {
+  const char* name;
+  int64_t launches;
+  double ms;
+};
+struct ProfPending {
+  int entry;
+  hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof;
+std::vector<ProfPending> g_pending;
+std::vector<hipEvent_t> g_spare;
+
+hipEvent_t take_event() {
+  if (!g_spare.empty()) {
+    hipEvent_t e = g_spare.back();
+    g_spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  int entry = -1;
+  hipEvent_t start = nullptr;
+  hipStream_t stream;
+  ProfScope(const char* name, hipStream_t s) : stream(s) {
+    if (!g_prof_on) return;
+    for (size_t i = 0; i < g_prof.size(); ++i)
+      if (std::strcmp(g_prof[i].name, name) == 0) entry = (int)i;
+    if (entry < 0) {
+      g_prof.push_back({name, 0, 0.0});
+      entry = (int)g_prof.size() - 1;
+    }
+    start = take_event();
+    if (start) (void)hipEventRecord(start, stream);
+  }
+  ~ProfScope() {
+    if (!g_prof_on || !start) return;
+    hipEvent_t stop = take_event();
+    if (!stop) return;
+    (void)hipEventRecord(stop, stream);
+    g_pending.push_back({entry, start, stop});
+  }
+};
+
+skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+#define SKV_TRY(expr)                 \
+  do {                                \
+    skv_status st_ = (expr);          \
+    if (st_ != SKV_OK) return st_;    \
+  } while (0)
+
+skv_status run_scoring(const Dims& d, ScoreArgs& a, hipStream_t s) {
+  {
+    ProfScope p("score_pass1", s);
+    SKV_TRY(hip_status(launch_score_pass1(d.dtype, (int)d.D, a, s)));
+  }
+  {
+    ProfScope p("lse_combine", s);
+    SKV_TRY(hip_status(launch_lse_combine(a, s)));
+  }
+  return SKV_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* speckv_status_string(skv_status status) {
+  switch (status) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_NULL: return "required pointer is NULL";
+    case SKV_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case SKV_ERR_DTYPE: return "unsupported element type";
+    case SKV_ERR_PARAM: return "parameter out of range";
+    case SKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SKV_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case SKV_ERR_ALIAS: return "output overlaps an input";
+    case SKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!out) return SKV_ERR_NULL;
+  if (C_max < 0) return SKV_ERR_PARAM;
+  *out = keep_count(d, C_max);
+  return SKV_OK;
+}
+
+skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t* out) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!out) return SKV_ERR_NULL;
+  if (C_max < 0) return SKV_ERR_PARAM;
+  const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
+  const int64_t n_pre = d.n_in - d.n_window;
+  size_t need = score_ws(d, units, G * (d.n_window + d.n_lookahead), n_pre).end;           // speckv_scores
+  need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)));                  // speckv_select
+  need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
+  if (d.n_window >= 1) need = std::max(need, specpc_ws(d, units).end);                         // specpc_token_scores
+  *out = need;
+  return SKV_OK;
+}
+
+skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!q_obs || !k || !scores) return SKV_ERR_NULL;
+  const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
+  if (n_obs < 1) return SKV_ERR_SHAPE;
+  if (!aligned(q_obs, 16) || !aligned(k, 16) || !aligned(scores, 4)) return SKV_ERR_ALIGN;
+  const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
+  const ScoreWs w = score_ws(d, units, G * n_obs, n_pre);
+  if (n_pre == 0) return SKV_OK;
+  if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ScoreArgs a{};
+  a.q = q_obs;
+  a.k = k;
+  a.q_head_stride = n_obs * d.D;
+  a.q_layer_stride = d.Hq * a.q_head_stride;
+  a.k_head_stride = d.stride;
+  a.k_layer_stride = d.Hkv * d.stride;
+  a.layer0 = 0;
+  a.n_units = (int32_t)units;
+  a.n_kv_heads = (int32_t)d.Hkv;
+  a.group = (int32_t)G;
+  a.rows_per_qhead = (int32_t)n_obs;
+  a.n_rows = (int32_t)(G * n_obs);
+  a.n_keys = (int32_t)n_pre;
+  const int kpb = score_keys_per_block(d.dtype, (int)d.D);
+  a.n_chunks = (int32_t)((n_pre + kpb - 1) / kpb);
+  a.causal = 0;
+  a.pos_base = 0;
+  a.c = d.scale * 1.4426950408889634f;
+  char* base = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float2*>(base + w.part);
+  a.lam = reinterpret_cast<float*>(base + w.lam);
+  a.scores = scores;
+  SKV_TRY(run_scoring(d, a, s));
+  ProfScope p("score_pass2", s);
+  return hip_status(launch_score_pass2(d.dtype, (int)d.D, a, s));
+}
+
+skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,
+                         int32_t* kept, float* pooled, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!scores || !kept) return SKV_ERR_NULL;
+  if (C_max < 0) return SKV_ERR_PARAM;
+  if (pool != SKV_POOL_NONE && pool != SKV_POOL_MAX && pool != SKV_POOL_AVG) return SKV_ERR_PARAM;
+  if (pool != SKV_POOL_NONE && (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 4097)) return SKV_ERR_PARAM;
+  if (!aligned(scores, 4) || !aligned(kept, 4) || (pooled && !aligned(pooled, 4))) return SKV_ERR_ALIGN;
+  const int64_t units = d.L * d.Hkv, n_pre = d.n_in - d.n_window;
+  const int64_t n_keep = keep_count(d, C_max);
+  if (pooled && ranges_overlap(pooled, (size_t)(units * n_pre) * 4, scores, (size_t)(units * n_pre) * 4))
+    return SKV_ERR_ALIAS;
+  if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, scores, (size_t)(units * n_pre) * 4)) return SKV_ERR_ALIAS;
+  float* pl = pooled;
+  if (!pl) {
+    if (!ws || ws_bytes < (size_t)(units * n_pre) * sizeof(float)) return SKV_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return SKV_ERR_ALIGN;
+    pl = static_cast<float*>(ws);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SelectArgs a{};
+  a.scores = scores;
+  a.pooled = pl;
+  a.kept = kept;
+  a.n_units = (int32_t)units;
+  a.n_pre = (int32_t)n_pre;
+  a.n_window = (int32_t)d.n_window;
+  a.n_top = (int32_t)(n_keep - d.n_window);
+  a.pool = pool;
+  a.pool_radius = pool == SKV_POOL_NONE ? 0 : pool_kernel / 2;
+  ProfScope p("select", s);
+  return hip_status(launch_select(a, s));
+}
+
+skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, const int32_t* kept, int64_t n_keep,
+                          void* k_out, void* v_out, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!k || !v || !kept || !k_out || !v_out) return SKV_ERR_NULL;
+  if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4))
+    return SKV_ERR_ALIGN;
+  const int64_t units = d.L * d.Hkv, row_bytes = d.D * d.esize;
+  const size_t in_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * row_bytes);
+  const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
+  const bool k_inplace = (k_out == k), v_inplace = (v_out == v);
+  if (k_inplace != v_inplace) return SKV_ERR_ALIAS;
+  if (k == v) return SKV_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GatherArgs g{};
+  g.n_units = (int32_t)units;
+  g.n_rows = (int32_t)n_keep;
+  g.n_src_rows = (int32_t)d.n_in;
+  g.row_bytes = (int32_t)row_bytes;
+  g.src_unit_stride = d.stride * d.esize;
+  if (!k_inplace) {
+    if (ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+        ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
+        ranges_overlap(k_out, out_bytes, v_out, out_bytes) ||
+        ranges_overlap(kept, (size_t)(units * n_keep) * 4, k_out, out_bytes) ||
+        ranges_overlap(kept, (size_t)(units * n_keep) * 4, v_out, out_bytes))
+      return SKV_ERR_ALIAS;
+    ProfScope p("compact_gather", s);
+    g.idx = kept;
+    g.dst_unit_stride = n_keep * row_bytes;
+    g.src = k;
+    g.dst = k_out;
+    SKV_TRY(hip_status(launch_gather(g, s)));
+    g.src = v;
+    g.dst = v_out;
+    return hip_status(launch_gather(g, s));
+  }
+  // In place: gather K and V into the workspace, then copy back to rows [0, n_keep).
+  if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, k, in_bytes) ||
+      ranges_overlap(kept, (size_t)(units * n_keep) * 4, v, in_bytes) || ranges_overlap(k, in_bytes, v, in_bytes))
+    return SKV_ERR_ALIAS;
+  const size_t stage = round_up(out_bytes);
+  if (!ws || ws_bytes < 2 * stage) return SKV_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+  if (ranges_overlap(ws, 2 * stage, k, in_bytes) || ranges_overlap(ws, 2 * stage, v, in_bytes)) return SKV_ERR_ALIAS;
+  char* ks = static_cast<char*>(ws);
+  char* vs = ks + stage;
+  {
+    ProfScope p("compact_gather", s);
+    g.idx = kept;
+    g.dst_unit_stride = n_keep * row_bytes;
+    g.src = k;
+    g.dst = ks;
+    SKV_TRY(hip_status(launch_gather(g, s)));
+    g.src = v;
+    g.dst = vs;
+    SKV_TRY(hip_status(launch_gather(g, s)));
+  }
+  ProfScope p("compact_copyback", s);
+  GatherArgs b{};
+  b.n_units = (int32_t)units;
+  b.n_rows = (int32_t)n_keep;
+  b.n_src_rows = (int32_t)n_keep;
+  b.row_bytes = (int32_t)row_bytes;
+  b.idx = nullptr;
+  b.src_unit_stride = n_keep * row_bytes;
+  b.dst_unit_stride = d.stride * d.esize;
+  b.src = ks;
+  b.dst = const_cast<void*>(k);
+  SKV_TRY(hip_status(launch_gather(b, s)));
+  b.src = vs;
+  b.dst = const_cast<void*>(v);
+  return hip_status(launch_gather(b, s));
+}
+
+skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,
+                               const float* query_weights, float* token_scores, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!q_win || !k || !token_scores) return SKV_ERR_NULL;
+  if (l_skip < 0 || l_skip >= d.L) return SKV_ERR_PARAM;
+  const int64_t W = d.n_window;
+  if (W < 1) return SKV_ERR_SHAPE;
+  if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(token_scores, 4) ||
+      (query_weights && !aligned(query_weights, 4)))
+    return SKV_ERR_ALIGN;
+  const int64_t G = d.Hq / d.Hkv, units = (d.L - l_skip) * d.Hkv;
+  const PcWs w = specpc_ws(d, units);
+  if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SpecPCArgs pa{};
+  ScoreArgs& a = pa.sc;
+  a.q = q_win;
+  a.k = k;
+  a.q_head_stride = W * d.D;
+  a.q_layer_stride = d.Hq * a.q_head_stride;
+  a.k_head_stride = d.stride;
+  a.k_layer_stride = d.Hkv * d.stride;
+  a.layer0 = l_skip;
+  a.n_units = (int32_t)units;
+  a.n_kv_heads = (int32_t)d.Hkv;
+  a.group = (int32_t)G;
+  a.rows_per_qhead = (int32_t)W;
+  a.n_rows = (int32_t)(G * W);
+  a.n_keys = (int32_t)d.n_in;
+  const int kpb = score_keys_per_block(d.dtype, (int)d.D);
+  a.n_chunks = (int32_t)((d.n_in + kpb - 1) / kpb);
+  a.causal = 1;
+  a.pos_base = d.n_in - W;
+  a.c = d.scale * 1.4426950408889634f;
+  char* base = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float2*>(base + w.sc.part);
+  a.lam = reinterpret_cast<float*>(base + w.sc.lam);
+  a.scores = nullptr;
+  pa.weights = query_weights;
+  pa.rowblock_max = reinterpret_cast<float*>(base + w.rowmax);
+  pa.token_scores = token_scores;
+  const int rpb = specpc_rows_per_block(d.dtype, (int)d.D);
+  pa.n_rowblocks = (int32_t)((W + rpb - 1) / rpb);
+  pa.inv_maps = (float)(1.0 / (double)(units * G));
+  SKV_TRY(run_scoring(d, a, s));
+  {
+    ProfScope p("specpc_pass2", s);
+    SKV_TRY(hip_status(launch_specpc_pass2(d.dtype, (int)d.D, pa, s)));
+  }
+  ProfScope p("specpc_reduce", s);
+  return hip_status(launch_specpc_reduce(pa, s));
+}
+
+skv_status speckv_profile_enable(int32_t on) {
+  if (on) {
+    g_prof.clear();
+    for (auto& p : g_pending) {
+      g_spare.push_back(p.start);
+      g_spare.push_back(p.stop);
+    }
+    g_pending.clear();
+  }
+  g_prof_on = on != 0;
+  return SKV_OK;
+}
+
+int32_t speckv_profile_count(void) { return (int32_t)g_prof.size(); }
+
+skv_status speckv_profile_read(int32_t index, const char** name, int64_t* launches, double* total_ms) {
+  for (auto& p : g_pending) {
+    if (hipEventSynchronize(p.stop) != hipSuccess) return SKV_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) return SKV_ERR_HIP;
+    g_prof[p.entry].launches += 1;
+    g_prof[p.entry].ms += ms;
+    g_spare.push_back(p.start);
+    g_spare.push_back(p.stop);
+  }
+  g_pending.clear();
+  if (index < 0 || index >= (int32_t)g_prof.size()) return SKV_ERR_PARAM;
+  if (name) *name = g_prof[index].name;
+  if (launches) *launches = g_prof[index].launches;
+  if (total_ms) *total_ms = g_prof[index].ms;
+  return SKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+// One scoring problem: units u = (layer, KV head); each unit has R query
+// rows (G query heads x rows_per_qhead) and n_keys scored keys.
+struct ScoreArgs {
+  const void* q;            // [layers][Hq][rows_per_qhead][D]
+  const void* k;            // [layers][Hkv][k_head_stride]
+  int64_t q_layer_stride;   // elements
+  int64_t q_head_stride;    // elements
+  int64_t k_layer_stride;   // elements
+  int64_t k_head_stride;    // elements
+  int32_t layer0;           // first layer scored (SpecPC: l_skip)
+  int32_t n_units;          // (layers - layer0) * Hkv
+  int32_t n_kv_heads;
+  int32_t group;            // G = Hq / Hkv
+  int32_t rows_per_qhead;   // SpecKV: n_window + n_lookahead; SpecPC: W
+  int32_t n_rows;           // R = G * rows_per_qhead
+  int32_t n_keys;           // SpecKV: n_pre; SpecPC: n_in
+  int32_t n_chunks;         // key chunks per unit (pass 1 partial count)
+  int32_t causal;           // SpecPC: row i sees keys j <= pos_base + i
+  int64_t pos_base;         // SpecPC: n_in - W
+  float c;                  // logit scale * log2(e)
+  float2* part;             // pass 1 output: [n_units][n_chunks][R] (max, sum) in log2 units
+  float* lam;               // combine output / pass 2 input: [n_units][R] log2-domain lse
+  float* scores;            // pass 2 output: [n_units][n_keys]
+};
+
+int score_keys_per_block(int dtype, int head_dim);
+hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
+
+// SpecPC pass 2: mean over (layer, query head) of the causal probabilities,
+// weighted max over window rows, per key.
+struct SpecPCArgs {
+  ScoreArgs sc;             // same problem description (causal), lam filled
+  const float* weights;     // [W] or nullptr (linear 0.1 .. 1)
+  float* rowblock_max;      // [n_rowblocks][n_in] partial maxima (workspace)
+  float* token_scores;      // [n_in]
+  int32_t n_rowblocks;
+  float inv_maps;           // 1 / ((L - l_skip) * Hq)
+};
+int specpc_rows_per_block(int dtype, int head_dim);
+int specpc_keys_per_block(int dtype, int head_dim);
+hipError_t launch_specpc_pass2(int dtype, int head_dim, const SpecPCArgs& a, hipStream_t s);
+hipError_t launch_specpc_reduce(const SpecPCArgs& a, hipStream_t s);
+
+// Pooling + top-k selection, one block per unit.
+struct SelectArgs {
+  const float* scores;      // [n_units][n_pre]
+  float* pooled;            // [n_units][n_pre]
+  int32_t* kept;            // [n_units][n_keep]
+  int32_t n_units;
+  int32_t n_pre;
+  int32_t n_window;
+  int32_t n_top;            // min(C_max, n_pre)
+  int32_t pool;             // skv_pool
+  int32_t pool_radius;      // pool_kernel / 2
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// Row gather: dst[u][t] = src[u][idx[u][t]] (or src[u][t] when idx is null).
+struct GatherArgs {
+  const void* src;
+  void* dst;
+  const int32_t* idx;       // [n_units][n_rows] or nullptr
+  int64_t src_unit_stride;  // bytes
+  int64_t dst_unit_stride;  // bytes
+  int32_t n_units;
+  int32_t n_rows;           // rows per unit to write
+  int32_t n_src_rows;       // valid source rows per unit (bounds check)
+  int32_t row_bytes;        // multiple of 16
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+}  // namespace skv

@@ -1,0 +1,235 @@
+// SpecPC token scoring, pass 2 (paper notes "Draft-based Approximate
+// Inference for LLMs", section "Key designs", SpecPC: the draft's attention
+// rows over a window of queries, layers below l_skip skipped, mean over
+// layers and heads first, then a weighted max over the window rows).
+//
+// The mean must be complete before the max, so each block keeps its
+// (window rows x keys) tile of the running sum
+//   acc[i][j] = sum over (layer, query head) of 2^(c <q_i, k_j> - lse_i)
+// in registers across all (layer, query head) pairs, with the keys of the
+// current (layer, KV head) resident as MFMA operands (shared by the G query
+// heads of the group) and the query rows streamed through LDS.  The
+// attention tensor itself is never stored.  At the end each lane owns one key
+// column: it takes the weighted max over its rows; a tiny second kernel
+// takes the max over row blocks and applies the 1 / (layers x heads) mean.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+
+namespace skv {
+
+template <typename T, int D>
+struct PcGeom {
+  using RF = RowFrag<T, D>;
+  static constexpr int kNV = RF::kNV;
+  static constexpr int kKT = 2;          // key tiles per wave
+  static constexpr int kRT = 2;          // row tiles per block (64 window rows)
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kKeysPerWave = 32 * kKT;
+  static constexpr int kKeysPerBlock = kWaves * kKeysPerWave;
+  static constexpr int kRowsPerBlock = 32 * kRT;
+  static constexpr int kRowPitch = RF::kRowBytes + 16;
+  static constexpr int kTileBytes = kRowsPerBlock * kRowPitch;
+  static constexpr int kVecPerRow = RF::kRowBytes / 16;
+  static constexpr int kStageVecs = kRowsPerBlock * kVecPerRow / kThreads;
+  static_assert((kRowsPerBlock * kVecPerRow) % kThreads == 0, "tile must split evenly over the block");
+};
+
+template <typename T, int D, bool MASKED>
+__global__ __launch_bounds__(256, 2) void specpc_pass2_kernel(SpecPCArgs pa, int kblock0, int n_kblocks_launch) {
+  using Gm = PcGeom<T, D>;
+  const ScoreArgs& a = pa.sc;
+  __shared__ __attribute__((aligned(16))) char s_tile[2][Gm::kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_lam[2][Gm::kRowsPerBlock];
+
+  // This launch covers key blocks [kblock0, kblock0 + n_kblocks_launch) of every row block.
+  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int rb = logical / n_kblocks_launch, kblk = kblock0 + logical % n_kblocks_launch;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, half = lane / 32;
+  const int W = a.rows_per_qhead;
+  const int row0 = rb * Gm::kRowsPerBlock;                    // first window row of the block
+  const int kbase = kblk * Gm::kKeysPerBlock + wave * Gm::kKeysPerWave;
+  const int n_iter = a.n_units * a.group;                     // (layer, KV head, group member)
+  const float c = a.c;
+
+  // Waves whose keys all lie after the last row's position see nothing (causal).
+  const int64_t last_pos = a.pos_base + (int64_t)(row0 + Gm::kRowsPerBlock - 1);
+  const bool wave_active = (int64_t)kbase <= last_pos && kbase < a.n_keys;
+
+  // Stage iteration `it`: query rows [row0, row0 + 64) of (layer, hq) and their lse.
+  auto load_stage = [&](int it, u32x4 (&st)[Gm::kStageVecs], float& lst) {
+    const int unit = it / a.group, g = it % a.group;
+    const int layer = a.layer0 + unit / a.n_kv_heads, kvh = unit % a.n_kv_heads;
+    const char* qh = static_cast<const char*>(a.q) +
+                     (layer * a.q_layer_stride + (int64_t)(kvh * a.group + g) * a.q_head_stride) * Elem<T>::kBytes;
+#pragma unroll
+    for (int p = 0; p < Gm::kStageVecs; ++p) {
+      const int idx = p * Gm::kThreads + threadIdx.x;
+      const int row = idx / Gm::kVecPerRow, col = idx % Gm::kVecPerRow;
+      const int i = row0 + row;
+      st[p] = (i < W) ? ldg16(qh + (int64_t)i * Gm::RF::kRowBytes + col * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (threadIdx.x < Gm::kRowsPerBlock) {
+      const int i = row0 + threadIdx.x;
+      lst = (i < W) ? a.lam[(int64_t)unit * a.n_rows + (int64_t)g * W + i] : INFINITY;
+    }
+  };
+  auto store_stage = [&](int buf, const u32x4 (&st)[Gm::kStageVecs], float lst) {
+#pragma unroll
+    for (int p = 0; p < Gm::kStageVecs; ++p) {
+      const int idx = p * Gm::kThreads + threadIdx.x;
+      const int row = idx / Gm::kVecPerRow, col = idx % Gm::kVecPerRow;
+      *reinterpret_cast<u32x4*>(s_tile[buf] + row * Gm::kRowPitch + col * 16) = st[p];
+    }
+    if (threadIdx.x < Gm::kRowsPerBlock) s_lam[buf][threadIdx.x] = lst;
+  };
+
+  f32x16 acc[Gm::kRT][Gm::kKT];
+#pragma unroll
+  for (int r = 0; r < Gm::kRT; ++r)
+#pragma unroll
+    for (int kt = 0; kt < Gm::kKT; ++kt) acc[r][kt] = f32x16{};
+
+  u32x4 kst[Gm::kKT][Gm::kNV];
+  u32x4 st[Gm::kStageVecs];
+  float lst = INFINITY;
+  load_stage(0, st, lst);
+  store_stage(0, st, lst);
+  __syncthreads();
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    const int unit = it / a.group;
+    if (it % a.group == 0 && wave_active) {
+      // New (layer, KV head): load this wave's resident keys.
+      const int layer = a.layer0 + unit / a.n_kv_heads, kvh = unit % a.n_kv_heads;
+      const char* kb = static_cast<const char*>(a.k) +
+                       (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
+#pragma unroll
+      for (int kt = 0; kt < Gm::kKT; ++kt) {
+        const int key = kbase + kt * 32 + (lane % 32);
+        const char* row = kb + (int64_t)key * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
+#pragma unroll
+        for (int v = 0; v < Gm::kNV; ++v)
+          kst[kt][v] = (key < a.n_keys) ? ldg16(row + v * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (it + 1 < n_iter) load_stage(it + 1, st, lst);
+
+    if (wave_active) {
+#pragma unroll
+      for (int r = 0; r < Gm::kRT; ++r) {
+        // Keys after a row's position start at -inf (causal mask), so they add 0.
+        f32x16 sacc[Gm::kKT];
+        if constexpr (!MASKED) {
+#pragma unroll
+          for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = f32x16{};
+        } else {
+          int64_t rel64 = a.pos_base + row0 + r * 32 + 4 * half - (kbase + (lane % 32));
+          rel64 = rel64 < -4096 ? -4096 : (rel64 > 4096 ? 4096 : rel64);
+          const int rel = (int)rel64;
+#pragma unroll
+          for (int kt = 0; kt < Gm::kKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              sacc[kt][i] = (kt * 32 - 8 * (i >> 2) - (i & 3) <= rel) ? 0.f : -INFINITY;
+        }
+        const char* trow = s_tile[buf] + (r * 32 + lane % 32) * Gm::kRowPitch + half * Gm::RF::kHalfBytes;
+#pragma unroll
+        for (int v = 0; v < Gm::kNV; ++v) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(trow + v * 16);
+#pragma unroll
+          for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = Mfma<T>::step(qv, kst[kt][v], sacc[kt]);
+        }
+        // sacc[kt][i] = <q_(row0 + 32 r + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
+        float lam[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lam[buf][r * 32 + 8 * g4 + 4 * half]);
+          lam[4 * g4 + 0] = l4[0];
+          lam[4 * g4 + 1] = l4[1];
+          lam[4 * g4 + 2] = l4[2];
+          lam[4 * g4 + 3] = l4[3];
+        }
+#pragma unroll
+        for (int kt = 0; kt < Gm::kKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[r][kt][i] += fast_exp2(__builtin_fmaf(sacc[kt][i], c, -lam[i]));
+        __builtin_amdgcn_sched_barrier(0);  // keep the two row tiles' live ranges apart
+      }
+    }
+    if (it + 1 < n_iter) store_stage(buf ^ 1, st, lst);
+    __syncthreads();
+  }
+
+  // Weighted max over this block's window rows, per key.
+  float wmax[Gm::kKT];
+#pragma unroll
+  for (int kt = 0; kt < Gm::kKT; ++kt) wmax[kt] = 0.f;
+#pragma unroll
+  for (int r = 0; r < Gm::kRT; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int wi = row0 + r * 32 + acc_row(i, half);
+      float w = 0.f;
+      if (wi < W) w = pa.weights ? pa.weights[wi] : (W == 1 ? 1.f : 0.1f + 0.9f * (float)wi / (float)(W - 1));
+#pragma unroll
+      for (int kt = 0; kt < Gm::kKT; ++kt) wmax[kt] = fmaxf(wmax[kt], w * acc[r][kt][i]);
+    }
+  float* out = pa.rowblock_max + (int64_t)rb * a.n_keys;
+#pragma unroll
+  for (int kt = 0; kt < Gm::kKT; ++kt) {
+    const float m = fmaxf(wmax[kt], shfl_xor32(wmax[kt]));
+    const int key = kbase + kt * 32 + lane;
+    if (lane < 32 && key < a.n_keys) out[key] = m;
+  }
+}
+
+__global__ __launch_bounds__(256) void specpc_reduce_kernel(SpecPCArgs pa) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= pa.sc.n_keys) return;
+  float m = 0.f;
+  for (int rb = 0; rb < pa.n_rowblocks; ++rb) m = fmaxf(m, pa.rowblock_max[(int64_t)rb * pa.sc.n_keys + j]);
+  pa.token_scores[j] = m * pa.inv_maps;
+}
+
+int specpc_rows_per_block(int, int) { return PcGeom<bf16_t, 64>::kRowsPerBlock; }
+
+int specpc_keys_per_block(int dtype, int head_dim) {
+  if (dtype == 0) return head_dim == 64 ? PcGeom<float, 64>::kKeysPerBlock : PcGeom<float, 128>::kKeysPerBlock;
+  return head_dim == 64 ? PcGeom<bf16_t, 64>::kKeysPerBlock : PcGeom<bf16_t, 128>::kKeysPerBlock;
+}
+
+template <typename T, int D>
+static void launch_pc2(const SpecPCArgs& a, hipStream_t s) {
+  using Gm = PcGeom<T, D>;
+  const int n_kblocks = (a.sc.n_keys + Gm::kKeysPerBlock - 1) / Gm::kKeysPerBlock;
+  // Key blocks whose every key precedes the first window position need no causal mask.
+  int64_t n_plain = (a.sc.pos_base + 1) / Gm::kKeysPerBlock;
+  if (n_plain > n_kblocks) n_plain = n_kblocks;
+  if ((int64_t)n_kblocks * Gm::kKeysPerBlock > a.sc.n_keys && n_plain == n_kblocks) n_plain = n_kblocks - 1;
+  const int n_masked = n_kblocks - (int)n_plain;
+  if (n_plain > 0)
+    specpc_pass2_kernel<T, D, false><<<dim3((unsigned)(n_plain * a.n_rowblocks)), dim3(Gm::kThreads), 0, s>>>(
+        a, 0, (int)n_plain);
+  if (n_masked > 0)
+    specpc_pass2_kernel<T, D, true><<<dim3((unsigned)(n_masked * a.n_rowblocks)), dim3(Gm::kThreads), 0, s>>>(
+        a, (int)n_plain, n_masked);
+}
+
+hipError_t launch_specpc_pass2(int dtype, int head_dim, const SpecPCArgs& a, hipStream_t s) {
+  if (dtype == 0 && head_dim == 64) launch_pc2<float, 64>(a, s);
+  else if (dtype == 0) launch_pc2<float, 128>(a, s);
+  else if (head_dim == 64) launch_pc2<bf16_t, 64>(a, s);
+  else launch_pc2<bf16_t, 128>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_specpc_reduce(const SpecPCArgs& a, hipStream_t s) {
+  specpc_reduce_kernel<<<dim3((unsigned)((a.sc.n_keys + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -203,9 +203,10 @@ def specpc_layer(cfg: SpecPCConfig, layer: int, seed: int, device="cpu"):
     gh = _gen(seed, layer, "hh", device)
     q_rounded = q.to(cfg.torch_dtype).float()
     u = _unit_mean_direction(q_rounded.reshape(Hkv, G * W, d))
-    n_pre = cfg.n_in - W
+    n_pre = cfg.n_in - W  # planted keys lie before the window
+    n_hh = min(cfg.n_in // 100, max(n_pre - 1, 0))
     for h in range(Hkv):
-        pos = torch.randperm(n_pre - 1, generator=gh, device=device)[:cfg.n_in // 100] + 1
+        pos = torch.randperm(max(n_pre - 1, 0), generator=gh, device=device)[:n_hh] + 1
         pos = torch.cat([torch.zeros(1, dtype=pos.dtype, device=device), pos])
         k[h, pos] = cfg.beta * math.sqrt(d) * u[h] + _randn((pos.numel(), d), gh, device)
     dt = cfg.torch_dtype

@@ -1,0 +1,159 @@
+/*
+ * speckv.h — C ABI of the MI355X (gfx950) SpecKV / SpecPC scoring library.
+ *
+ * The operations follow the paper notes "Draft-based Approximate Inference
+ * for LLMs" (ICLR 2026 notes page):
+ *   - section "Key designs", SpecKV paragraph: per attention head, the
+ *     importance of each KV pair is the cross-attention of the observation
+ *     queries (the last n_window input tokens plus the n_lookahead draft
+ *     tokens) against the remaining input keys; the top C_max pairs are kept
+ *     together with the window's pairs;
+ *   - section "Key designs", SpecPC paragraph: token importance from the
+ *     draft's attention activations over a window of queries with weights
+ *     that fall away from the end, skipping the first l_skip layers, mean
+ *     first and then max;
+ *   - section "Loss / training strategy": local pooling keeps the kept
+ *     tokens contiguous.
+ *
+ * Conventions shared by every entry point
+ *   - All buffer pointers are DEVICE pointers owned by the caller, including
+ *     the workspace.  The library allocates and frees no device memory.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns; outputs are valid once the stream has
+ *     completed.  Calls that share one workspace must be ordered on one
+ *     stream.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is launched and the outputs are untouched.  No C++
+ *     exception crosses this interface.
+ *   - NaN or Inf inputs give undefined (but memory-safe) results.
+ *   - Element types: SKV_F32 (float) or SKV_BF16 (bfloat16 stored as
+ *     uint16).  head_dim must be 64 or 128.  Device pointers must be 16-byte
+ *     aligned, and kv_head_stride * element size must be a multiple of 16.
+ */
+#ifndef SPECKV_H
+#define SPECKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum skv_status {
+  SKV_OK = 0,
+  SKV_ERR_NULL = 1,      /* a required pointer is NULL                           */
+  SKV_ERR_SHAPE = 2,     /* sizes inconsistent, out of range or unsupported      */
+  SKV_ERR_DTYPE = 3,     /* unsupported element type                             */
+  SKV_ERR_PARAM = 4,     /* C_max, pooling, l_skip or n_keep out of range        */
+  SKV_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query returns     */
+  SKV_ERR_ALIGN = 6,     /* a pointer or the head stride is not 16-byte aligned  */
+  SKV_ERR_ALIAS = 7,     /* outputs overlap inputs other than the in-place form  */
+  SKV_ERR_HIP = 8        /* a HIP runtime call or kernel launch failed           */
+} skv_status;
+
+typedef enum skv_dtype { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+typedef enum skv_pool { SKV_POOL_NONE = 0, SKV_POOL_MAX = 1, SKV_POOL_AVG = 2 } skv_pool;
+
+/* Problem shape.  Layouts (row-major, head_dim contiguous):
+ *   K, V   : [n_layers][n_kv_heads][kv_head_stride]; head slab h of layer l
+ *            holds n_in rows of head_dim elements, rows beyond n_in unused.
+ *   SpecKV : Q_obs [n_layers][n_q_heads][n_window + n_lookahead][head_dim],
+ *            window rows first, then lookahead rows.
+ *   SpecPC : Q_win [n_layers][n_q_heads][n_window][head_dim]; row i is the
+ *            query of input position n_in - n_window + i.
+ * Query head hq uses KV head hq / (n_q_heads / n_kv_heads). */
+typedef struct skv_shape {
+  int32_t n_layers;       /* >= 1                                                   */
+  int32_t n_q_heads;      /* multiple of n_kv_heads                                 */
+  int32_t n_kv_heads;     /* >= 1                                                   */
+  int32_t head_dim;       /* 64 or 128                                              */
+  int64_t n_in;           /* input tokens (K/V rows per head), 1 .. 2^31 - 1        */
+  int64_t kv_head_stride; /* elements between head slabs; 0 means n_in * head_dim   */
+  int32_t n_window;       /* SpecKV: window rows (0 .. n_in); SpecPC: W (1 .. n_in) */
+  int32_t n_lookahead;    /* SpecKV: draft rows (>= 0); SpecPC: 1                   */
+  float scale;            /* logit scale; 0 means 1 / sqrt(head_dim)                */
+  int32_t dtype;          /* skv_dtype of Q, K and V                                */
+} skv_shape;
+
+/* Human-readable name of a status code (static storage). */
+const char* speckv_status_string(skv_status status);
+
+/* Workspace bytes that suffice for every entry point below on this shape
+ * (SpecKV with the given C_max, or SpecPC when called as such).  The same
+ * workspace may be reused by consecutive calls on one stream. */
+skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t* out_bytes);
+
+/* Kept rows per head: min(C_max, n_in - n_window) + n_window (SpecKV, key
+ * designs paragraph: the top C_max pairs plus the window pairs). */
+skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out_n_keep);
+
+/* SpecKV importance scores ("Key designs", SpecKV).
+ * For every layer l and KV head h, with rows r = (query head g of the group,
+ * observation row i) and the n_pre = n_in - n_window remaining input keys:
+ *   P[r][j]  = softmax over j < n_pre of scale * <q_r, k_j>
+ *   score[j] = sum over r of P[r][j]
+ * Inputs : q_obs (see skv_shape), k.
+ * Output : scores float [n_layers][n_kv_heads][n_pre] (raw sums; they total
+ *          G * (n_window + n_lookahead) per head).
+ * Requires n_pre >= 1 and n_window + n_lookahead >= 1. */
+skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* SpecKV selection ("Key designs", SpecKV; "Loss / training strategy",
+ * local pooling).  Per head: pooled = pool1d(scores) over the n_pre prefix
+ * scores (stride 1, odd pool_kernel, windows truncated at both ends; max or
+ * in-range mean; SKV_POOL_NONE copies); then the min(C_max, n_pre) best
+ * prefix keys, ordered by pooled score descending and lower index first on
+ * ties, plus every window key n_pre .. n_in - 1; written ascending.
+ * Inputs : scores float [n_layers][n_kv_heads][n_pre] (non-negative).
+ * Outputs: kept int32 [n_layers][n_kv_heads][n_keep]; pooled float
+ *          [n_layers][n_kv_heads][n_pre] or NULL.
+ * The SpecPC token selection is this call on a shape with n_layers = 1,
+ * n_kv_heads = 1 (n_q_heads = 1), n_in = tokens, n_window = 0. */
+skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool,
+                         int32_t pool_kernel, int32_t* kept, float* pooled, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* SpecKV compaction ("Key designs", SpecKV: keep the selected KV pairs).
+ * Per head: out[t] = in[kept[t]] for t < n_keep, for K and V, bit-exact.
+ * Out of place: k_out, v_out are [n_layers][n_kv_heads][n_keep][head_dim]
+ *   and must not overlap k or v.
+ * In place: k_out == k and v_out == v; rows 0 .. n_keep - 1 of every head
+ *   slab are overwritten, the stride is unchanged and rows >= n_keep are
+ *   left unspecified.  Requires kept ascending (as speckv_select writes it).
+ * kept values must lie in [0, n_in); n_keep in 1 .. n_in. */
+skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, const int32_t* kept,
+                          int64_t n_keep, void* k_out, void* v_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* SpecPC token scores ("Key designs", SpecPC).
+ * For layers l_skip <= l < n_layers and every query head hq, window row i
+ * (position p_i = n_in - W + i, W = n_window) attends causally:
+ *   P[l][hq][i][j] = softmax over j <= p_i of scale * <q_i, k_j>, 0 for j > p_i
+ *   Abar[i][j]     = mean over (l, hq) of P
+ *   token_scores[j] = max over i of w_i * Abar[i][j]
+ * query_weights: float [W] on the device, or NULL for w_i = 0.1 + 0.9 i/(W-1)
+ * (1 at the end of the window, 0.1 at its far edge; 1 when W = 1).
+ * Inputs : q_win [n_layers][n_q_heads][W][head_dim] (all layers, skipped
+ *          ones included), k.  Output: token_scores float [n_in].
+ * Requires 0 <= l_skip < n_layers and 1 <= W <= n_in. */
+skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,
+                               const float* query_weights, float* token_scores, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Optional per-kernel timing with HIP events, for measurement only.
+ * While enabled, every kernel the library launches is bracketed by a pair
+ * of events on its stream.  speckv_profile_read synchronizes on the
+ * recorded events and reports, per kernel name, the launch count and the
+ * summed event time.  Process-wide state, not thread-safe; off by default. */
+skv_status speckv_profile_enable(int32_t on);
+int32_t speckv_profile_count(void);
+skv_status speckv_profile_read(int32_t index, const char** name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECKV_H */

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: importance scores within 1e-3 relative (plus 1e-12 G n_obs
+absolute for values near fp32 underflow); kept sets identical except at
+keys whose pooled score ties the cut-off within that tolerance, and exactly
+equal to the selection rule applied to the GPU's own fp32 pooled scores;
+compacted K/V bit-exact for the kept indices.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_importance_scoring_amd as skv
+import oracle
+from attention_importance_scoring_amd import workloads as wl
+
+from gpu_helpers import (assert_compacted, assert_kept_matches, assert_scores_close, np64, run_speckv, shape_of,
+                         workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _to(inp, device):
+    out = dict(inp)
+    for key in ("q_obs", "k", "v", "k_buf", "v_buf"):
+        out[key] = inp[key].to(device)
+    d = inp["k"].shape[-1]
+    n_in = inp["k"].shape[2]
+    out["k"] = out["k_buf"][:, :, :n_in * d].unflatten(2, (n_in, d))
+    out["v"] = out["v_buf"][:, :, :n_in * d].unflatten(2, (n_in, d))
+    return out
+
+
+def _full_check(cfg, seed, C_max=None, pool_kernel=None, kv_head_stride=None, pool="max"):
+    print(f"\n[case] {cfg.name} L={cfg.n_layers} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim} "
+          f"{cfg.dtype} n_in={cfg.n_in} win={cfg.n_window} look={cfg.n_lookahead} seed={seed}", flush=True)
+    C_max = cfg.C_max if C_max is None else C_max
+    pool_kernel = cfg.pool_kernel if pool_kernel is None else pool_kernel
+    host = wl.speckv_inputs(cfg, seed, "cpu", kv_head_stride=kv_head_stride)
+    inp = _to(host, "cuda")
+    pool_id = {"max": skv.SKV_POOL_MAX, "avg": skv.SKV_POOL_AVG, "none": skv.SKV_POOL_NONE}[pool]
+    out = run_speckv(cfg, inp, C_max=C_max, pool=pool_id, pool_kernel=pool_kernel)
+    torch.cuda.synchronize()
+    q, k = np64(host["q_obs"]), np64(host["k"])
+    want = oracle.speckv_scores(q, k, cfg.n_window)
+    got = out["scores"].cpu().numpy()
+    assert_scores_close(got, want, cfg.G, cfg.n_obs)
+    # pooling of the GPU's own scores: exact for max (a max of fp32 values is exact)
+    pooled_gpu = out["pooled"].cpu().numpy()
+    ref_pool = oracle.pool1d(got.astype(np.float64), pool_kernel, pool)
+    if pool == "avg":
+        np.testing.assert_allclose(pooled_gpu, ref_pool, rtol=1e-5)
+    else:
+        np.testing.assert_array_equal(pooled_gpu.astype(np.float64), ref_pool)
+    pooled_oracle = oracle.pool1d(want, pool_kernel, pool)
+    kept = out["kept"].cpu().numpy()
+    L, H = kept.shape[:2]
+    assert_kept_matches(kept.reshape(L * H, -1), pooled_gpu.reshape(L * H, -1), pooled_oracle.reshape(L * H, -1),
+                        C_max, cfg.n_window)
+    assert_compacted(out["k_c"], out["v_c"], inp["k"], inp["v"], out["kept"])
+    return out
+
+
+def test_config1_tiny_fp32_full():
+    _full_check(wl.CONFIGS[1], seed=1)
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_in=1000, n_window=7, n_lookahead=5, C_max=100),
+    dict(n_layers=1, n_q_heads=14, n_kv_heads=2, head_dim=64, n_in=1537, n_window=33, n_lookahead=31, C_max=64),
+    dict(n_layers=1, n_q_heads=5, n_kv_heads=1, head_dim=128, n_in=700, n_window=32, n_lookahead=0, C_max=50),
+    dict(n_layers=1, n_q_heads=4, n_kv_heads=4, head_dim=64, n_in=513, n_window=1, n_lookahead=40, C_max=511),
+    dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, n_in=300, n_window=20, n_lookahead=3, C_max=1000),
+    dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_in=300, n_window=20, n_lookahead=3, C_max=0),
+], ids=["ragged-bf16-d128", "gqa7-d64", "window-only", "mha-cmax-npre", "cmax-above-npre", "cmax-zero"])
+def test_small_bf16_shapes(case):
+    cfg = wl.reduced(wl.CONFIGS[2], **case)
+    _full_check(cfg, seed=11)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64)])
+def test_other_dtype_headdim_combinations(dtype, d):
+    cfg = wl.reduced(wl.CONFIGS[1], dtype=dtype, head_dim=d, n_in=1100, n_q_heads=6, n_kv_heads=2)
+    _full_check(cfg, seed=3)
+
+
+def test_padded_head_stride_and_avg_pool():
+    cfg = wl.reduced(wl.CONFIGS[2], n_layers=2, n_in=900, C_max=77)
+    _full_check(cfg, seed=4, kv_head_stride=900 * 128 + 64, pool="avg", pool_kernel=5)
+
+
+def test_no_pooling():
+    cfg = wl.reduced(wl.CONFIGS[2], n_layers=1, n_in=1200, C_max=90)
+    _full_check(cfg, seed=5, pool="none", pool_kernel=1)
+
+
+def test_exact_ties_take_lowest_index():
+    # identical key rows give bit-identical scores; with no pooling the cut falls inside
+    # the tie and both sides must keep the lowest indices.
+    cfg = wl.reduced(wl.CONFIGS[2], n_layers=1, n_kv_heads=1, n_q_heads=4, n_in=600, n_window=16, n_lookahead=16,
+                     C_max=40, heavy_hitters="none")
+    host = wl.speckv_inputs(cfg, 6, "cpu")
+    kb = host["k_buf"].view(1, 1, 600, 128)
+    kb[0, 0, 100:200] = kb[0, 0, 5]  # 101 identical keys, the strongest by construction below
+    q = host["q_obs"].float()
+    u = q[0].reshape(-1, 128).mean(0)
+    kb[0, 0, 100:200] = (3.0 * math.sqrt(128) * u / u.norm()).to(torch.bfloat16)
+    kb[0, 0, 5] = kb[0, 0, 100]
+    inp = _to(host, "cuda")
+    out = run_speckv(cfg, inp, pool=skv.SKV_POOL_NONE, pool_kernel=1)
+    kept = out["kept"].cpu().numpy()[0, 0]
+    assert kept[:40].tolist() == [5] + list(range(100, 139))
+    scores = out["scores"].cpu().numpy()[0, 0]
+    assert len(set(scores[100:200].tolist())) == 1 and scores[5] == scores[100]
+    want = oracle.speckv_scores(np64(host["q_obs"]), np64(host["k"]), cfg.n_window)
+    assert oracle.select_kept(want[0, 0], 40, 16).tolist() == kept.tolist()
+
+
+def test_in_place_equals_out_of_place_and_deterministic():
+    cfg = wl.reduced(wl.CONFIGS[4], n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
+    host = wl.speckv_inputs(cfg, 7, "cpu")
+    a = run_speckv(cfg, _to(host, "cuda"))
+    b = run_speckv(cfg, _to(host, "cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(a["scores"], b["scores"]) and torch.equal(a["kept"], b["kept"])  # bitwise repeatable
+    inp = _to(host, "cuda")
+    k0, v0 = inp["k"].clone(), inp["v"].clone()
+    c = run_speckv(cfg, inp, in_place=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c["k_c"], a["k_c"]) and torch.equal(c["v_c"], a["v_c"])
+    assert_compacted(c["k_c"], c["v_c"], k0, v0, c["kept"])
+
+
+def test_config2_llama_shape_two_layers_full_length():
+    cfg = wl.CONFIGS[2]
+    print("\n[case] config 2, layers 0 and 31, n_in=16384", flush=True)
+    host = wl.speckv_inputs(cfg, 2, "cpu", layers=[0, 31])
+    inp = _to(host, "cuda")
+    red = wl.reduced(cfg, n_layers=2)
+    out = run_speckv(red, inp)
+    torch.cuda.synchronize()
+    want = oracle.speckv_scores(np64(host["q_obs"]), np64(host["k"]), cfg.n_window)
+    assert_scores_close(out["scores"].cpu().numpy(), want, cfg.G, cfg.n_obs)
+    pooled_o = oracle.pool1d(want, 7, "max")
+    kept = out["kept"].cpu().numpy()
+    assert_kept_matches(kept.reshape(16, -1), out["pooled"].cpu().numpy().reshape(16, -1), pooled_o.reshape(16, -1),
+                        cfg.C_max, cfg.n_window)
+    assert_compacted(out["k_c"], out["v_c"], inp["k"], inp["v"], out["kept"])
+
+
+def _specpc_check(cfg, seed, weights=None):
+    print(f"\n[case] specpc L={cfg.n_layers} l_skip={cfg.l_skip} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} "
+          f"d={cfg.head_dim} {cfg.dtype} n_in={cfg.n_in} W={cfg.window} seed={seed}", flush=True)
+    host = wl.specpc_inputs(cfg, seed, "cpu")
+    dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
+    shape = skv.make_shape(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_in, cfg.window,
+                           cfg.n_lookahead, dt)
+    ws = workspace(shape, 0)
+    q, k = host["q_win"].cuda(), host["k"].cuda()
+    ts = torch.full((cfg.n_in,), float("nan"), dtype=torch.float32, device="cuda")
+    wt = None if weights is None else torch.as_tensor(weights, dtype=torch.float32, device="cuda")
+    skv.specpc_token_scores(shape, cfg.l_skip, q, k, wt, ts, ws)
+    sel_shape = skv.make_shape(1, 1, 1, cfg.head_dim, cfg.n_in, 0, 0, dt)
+    kept = torch.full((min(cfg.k_top, cfg.n_in),), -1, dtype=torch.int32, device="cuda")
+    pooled = torch.empty_like(ts)
+    skv.speckv_select(sel_shape, ts, cfg.k_top, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws)
+    torch.cuda.synchronize()
+    want = oracle.specpc_token_scores(np64(host["q_win"]), np64(host["k"]), cfg.l_skip,
+                                      None if weights is None else np.asarray(weights, dtype=np.float64))
+    assert_scores_close(ts.cpu().numpy(), want, cfg.G, cfg.window, "token scores")
+    pooled_o = oracle.pool1d(want, cfg.pool_kernel, "max")
+    assert_kept_matches(kept.cpu().numpy()[None], pooled.cpu().numpy()[None], pooled_o[None], cfg.k_top, 0,
+                        "tokens")
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_layers=3, l_skip=1, n_in=1000, window=100, k_top=64),
+    dict(n_layers=2, l_skip=0, n_in=777, window=1, k_top=700),
+    dict(n_layers=2, l_skip=1, n_in=300, window=300, k_top=30),
+], ids=["ragged", "single-window-row", "window-equals-input"])
+def test_specpc_small(case):
+    _specpc_check(wl.reduced(wl.CONFIGS[5], **case), seed=21)
+
+
+def test_specpc_user_weights_and_fp32():
+    cfg = wl.reduced(wl.CONFIGS[5], n_layers=2, l_skip=1, n_in=640, window=70, k_top=50, dtype="f32")
+    w = np.random.default_rng(0).random(70) + 0.05
+    _specpc_check(cfg, seed=22, weights=w)
+
+
+def test_specpc_config5_two_used_layers_full_length():
+    # full n_in and W of the draft workload with 2 of the 20 used layers
+    _specpc_check(wl.reduced(wl.CONFIGS[5], n_layers=6), seed=5)
