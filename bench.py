@@ -1,0 +1,281 @@
+"""Throughput of the SpecKV scoring + selection + compaction path on one MI355X.
+
+One step = speckv_scores + speckv_select + speckv_compact over every layer
+and KV head of the workload (default: the Qwen2.5-32B-shaped 64K-token
+workload: 64 layers, 40 query / 8 KV heads, head_dim 128, bf16, 32 window +
+128 lookahead queries, C_max 256, max-pool 7).  Inputs are synthetic, seeded
+and resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+--gpus N with N > 1 is refused: the path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "keys scored+compacted/sec and % of HBM/MFMA roofline at n_in=64K, 32B shape"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["attention_importance_scoring_amd/csrc/" + f for f in
+                  ("common.hpp", "kernels.hpp", "score.hip", "select.hip", "specpc.hip", "capi.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen32b_shape_64k",
+                   choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration runs)")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def speckv_cpu_baseline(cfg, inp, budget_s=12.0):
+    """The fp64 oracle (scores, pooling, selection, compaction) on whole
+    (layer, KV head) units of the same workload, until ~budget_s of work."""
+    import numpy as np
+    import torch
+    import oracle
+    from attention_importance_scoring_amd import workloads as wl
+    G = cfg.G
+    done, keys, t_total = 0, 0, 0.0
+    L = inp["q_obs"].shape[0]
+    units = [(l, h) for l in range(L) for h in range(cfg.n_kv_heads)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(units))
+    for idx in order:
+        l, h = units[idx]
+        q = wl.to_numpy_f64(inp["q_obs"][l, h * G:(h + 1) * G])
+        k = wl.to_numpy_f64(inp["k"][l, h])
+        v = inp["v"][l, h].cpu()
+        v_raw = v.view(torch.int16).numpy() if v.dtype == torch.bfloat16 else v.numpy()  # bit copy
+        t0 = time.perf_counter()
+        s = oracle.head_scores(q, k[:cfg.n_pre], oracle.default_scale(cfg.head_dim))
+        pooled = oracle.pool1d(s, cfg.pool_kernel, "max")
+        kept = oracle.select_kept(pooled, cfg.C_max, cfg.n_window)
+        oracle.compact_rows(k, kept)
+        oracle.compact_rows(v_raw, kept)
+        t_total += time.perf_counter() - t0
+        done += 1
+        keys += cfg.n_in
+        if t_total >= budget_s:
+            break
+    return {"value": keys / t_total, "unit": "keys/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (layer, KV head) units of the same workload, {keys} keys, "
+                      f"{t_total:.1f} s of fp64 NumPy"}
+
+
+def traffic_for(kernel: str, per_launch_alg_bytes=None):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it is absent or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def bench_speckv(args, cfg, torch, skv, wl):
+    from_layers = None
+    dev = "cuda"
+    t0 = time.perf_counter()
+    inp = wl.speckv_inputs(cfg, seed=args.seed or 3, device=dev, layers=from_layers)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
+    per_layer = cfg.in_place  # the in-place workload keeps one layer's cache per call
+    call_layers = 1 if per_layer else L
+    shape = skv.make_shape(call_layers, cfg.n_q_heads, H, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, dt)
+    ws = torch.empty(skv.speckv_workspace_bytes(shape, cfg.C_max), dtype=torch.uint8, device=dev)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    scores = torch.empty((L, H, cfg.n_pre), dtype=torch.float32, device=dev)
+    pooled = torch.empty_like(scores)
+    kept = torch.empty((L, H, n_keep), dtype=torch.int32, device=dev)
+    kc = torch.empty((L, H, n_keep, d), dtype=inp["k"].dtype, device=dev) if not per_layer else None
+    vc = torch.empty_like(kc) if kc is not None else None
+    stream = torch.cuda.current_stream()
+    kbuf, vbuf = inp["k_buf"], inp["v_buf"]
+
+    def step():
+        if not per_layer:
+            skv.speckv_scores(shape, inp["q_obs"], kbuf, scores, ws, stream)
+            skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws, stream)
+            skv.speckv_compact(shape, kbuf, vbuf, kept, n_keep, kc, vc, ws, stream)
+        else:
+            for layer in range(L):
+                skv.speckv_scores(shape, inp["q_obs"][layer:layer + 1], kbuf[layer:layer + 1], scores[layer:layer + 1],
+                                  ws, stream)
+                skv.speckv_select(shape, scores[layer:layer + 1], cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel,
+                                  kept[layer:layer + 1], pooled[layer:layer + 1], ws, stream)
+                skv.speckv_compact(shape, kbuf[layer:layer + 1], vbuf[layer:layer + 1], kept[layer:layer + 1], n_keep,
+                                   kbuf[layer:layer + 1], vbuf[layer:layer + 1], ws, stream)
+
+    print(f"[bench] inputs ready ({gen_s:.1f} s); warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    skv.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = skv.profile_read()
+    skv.profile_enable(False)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    keys = cfg.keys_per_call
+    R = cfg.G * cfg.n_obs
+    flops_per_pass = 2.0 * R * cfg.n_pre * d * L * H   # one Q_obs K^T over every head
+    kern = {name: {"launches": n, "avg_ms": t / max(n, 1), "ms_per_step": t / args.steps} for name, (n, t) in prof.items()}
+    # dominant kernel: the longer of the two scoring passes (each computes one Q_obs K^T)
+    dom = max(("score_pass1", "score_pass2"), key=lambda k: kern[k]["ms_per_step"])
+    launches_per_step = kern[dom]["launches"] / args.steps
+    flops_per_launch = flops_per_pass / launches_per_step
+    avg_s = kern[dom]["avg_ms"] * 1e-3
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    achieved = flops_per_launch / avg_s / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom)}
+    # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
+    path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
+    out = {
+        "metric": METRIC, "value": keys / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "n_layers": L, "n_q_heads": cfg.n_q_heads, "n_kv_heads": H, "head_dim": d,
+                   "n_in": cfg.n_in, "n_window": cfg.n_window, "n_lookahead": cfg.n_lookahead, "C_max": cfg.C_max,
+                   "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys},
+        "roofline": roof,
+        "path_mfma_frac": round(path_frac, 4),
+        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "ms_per_step": round(v["ms_per_step"], 4)}
+                    for k, v in kern.items()},
+    }
+    return out, inp
+
+
+def bench_specpc(args, cfg, torch, skv, wl):
+    dev = "cuda"
+    inp = wl.specpc_inputs(cfg, seed=args.seed or 5, device=dev)
+    dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
+    shape = skv.make_shape(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_in, cfg.window,
+                           cfg.n_lookahead, dt)
+    sel = skv.make_shape(1, 1, 1, cfg.head_dim, cfg.n_in, 0, 0, dt)
+    ws = torch.empty(skv.speckv_workspace_bytes(shape, 0), dtype=torch.uint8, device=dev)
+    ts = torch.empty(cfg.n_in, dtype=torch.float32, device=dev)
+    pooled = torch.empty_like(ts)
+    kept = torch.empty(cfg.k_top, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        skv.specpc_token_scores(shape, cfg.l_skip, inp["q_win"], inp["k"], None, ts, ws, stream)
+        skv.speckv_select(sel, ts, cfg.k_top, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    skv.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = skv.profile_read()
+    skv.profile_enable(False)
+    kern = {name: {"avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
+            for name, (n, t) in prof.items()}
+    maps = (cfg.n_layers - cfg.l_skip) * cfg.n_q_heads
+    elems = maps * sum(min(cfg.n_in, cfg.n_in - cfg.window + i + 1) for i in range(cfg.window))
+    exps_per_s = 2 * elems / (ms * 1e-3)  # two passes, one exp per (row, visible key) each
+    return {
+        "metric": "SpecPC tokens scored+selected/sec (draft attention stack)", "value": cfg.n_in / (ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "l_skip": cfg.l_skip, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "n_in": cfg.n_in, "window": cfg.window,
+                   "k_top": cfg.k_top},
+        "exp_rate_per_s": exps_per_s, "kernels": kern,
+    }, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the scoring path is per-GPU work with no collectives "
+              "(see DESIGN.md for how it would shard); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import attention_importance_scoring_amd as skv
+    from attention_importance_scoring_amd import _lib
+    from attention_importance_scoring_amd import workloads as wl
+    _lib.load()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = {c.name: c for c in wl.CONFIGS.values()}[args.workload]
+    if args.workload == "specpc_draft_32k":
+        out, inp = bench_specpc(args, cfg, torch, skv, wl)
+    else:
+        out, inp = bench_speckv(args, cfg, torch, skv, wl)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n
+    if not args.no_cpu_baseline and args.workload != "specpc_draft_32k":
+        print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = speckv_cpu_baseline(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+"""C ABI on the host (no GPU needed): the library loads, exports every
+symbol include/speckv.h declares, and rejects bad arguments with the
+documented status before any HIP call is made.  Pointers passed here are
+fake and never dereferenced: every case fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_importance_scoring_amd as skv
+from attention_importance_scoring_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "speckv.h")
+
+OK, NULL, SHAPE, DTYPE, PARAM, WS, ALIGN, ALIAS = 0, 1, 2, 3, 4, 5, 6, 7
+P = ctypes.c_void_p
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec(?:kv|pc)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libspeckv.so is not built: run __graft_entry__.build()")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.speckv_status_string(code)
+    assert lib.speckv_status_string(99) == b"unknown status"
+
+
+def shape(**kw):
+    base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_in=1000, n_window=16, n_lookahead=8,
+                dtype=skv.SKV_BF16)
+    base.update(kw)
+    return skv.make_shape(**base)
+
+
+def _ws_bytes(lib, s, C_max=64):
+    out = ctypes.c_size_t()
+    st = lib.speckv_workspace_bytes(ctypes.byref(s), C_max, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), DTYPE),
+    (dict(n_q_heads=6, n_kv_heads=4), SHAPE),
+    (dict(head_dim=96), SHAPE),
+    (dict(n_window=1001), SHAPE),
+    (dict(n_window=-1), SHAPE),
+    (dict(n_lookahead=-2), SHAPE),
+    (dict(n_in=0), SHAPE),
+    (dict(n_layers=0), SHAPE),
+    (dict(kv_head_stride=1000 * 128 - 8), SHAPE),
+    (dict(kv_head_stride=1000 * 128 + 4), ALIGN),
+    (dict(scale=-1.0), PARAM),
+])
+def test_shape_validation(lib, kw, status):
+    s = shape(**kw)
+    assert _ws_bytes(lib, s)[0] == status
+    n = ctypes.c_int64()
+    assert lib.speckv_n_keep(ctypes.byref(s), 10, ctypes.byref(n)) == status
+    assert lib.speckv_scores(ctypes.byref(s), P(256), P(512), P(1024), P(4096), 1 << 30, None) == status
+
+
+def test_null_shape_and_outputs(lib):
+    assert lib.speckv_workspace_bytes(None, 1, ctypes.byref(ctypes.c_size_t())) == NULL
+    s = shape()
+    assert lib.speckv_scores(ctypes.byref(s), None, P(512), P(1024), P(4096), 1 << 30, None) == NULL
+    assert lib.speckv_select(ctypes.byref(s), P(256), 10, 1, 7, None, None, P(4096), 1 << 30, None) == NULL
+    assert lib.speckv_compact(ctypes.byref(s), P(256), None, P(4096), 10, P(8192), P(16384), None, 0, None) == NULL
+    assert lib.specpc_token_scores(ctypes.byref(s), 0, P(256), P(512), None, None, P(4096), 1 << 30, None) == NULL
+
+
+def test_n_keep_and_workspace_closed_forms(lib):
+    s = shape()
+    for C_max, want in ((0, 16), (64, 80), (984, 1000), (5000, 1000)):
+        n = ctypes.c_int64()
+        assert lib.speckv_n_keep(ctypes.byref(s), C_max, ctypes.byref(n)) == OK and n.value == want
+    st, nbytes = _ws_bytes(lib, s, 64)
+    assert st == OK
+    # at least the in-place staging of the kept K and V rows, and the per-head pooled scores
+    assert nbytes >= 2 * 2 * 2 * 80 * 128 * 2 and nbytes >= 2 * 2 * 984 * 4
+    assert lib.speckv_n_keep(ctypes.byref(s), -1, ctypes.byref(ctypes.c_int64())) == PARAM
+
+
+def test_scores_rejects_bad_pointers_and_workspace(lib):
+    s = shape()
+    _, nbytes = _ws_bytes(lib, s)
+    assert lib.speckv_scores(ctypes.byref(s), P(257), P(512), P(1024), P(4096), nbytes, None) == ALIGN
+    assert lib.speckv_scores(ctypes.byref(s), P(256), P(520), P(1024), P(4096), nbytes, None) == ALIGN
+    assert lib.speckv_scores(ctypes.byref(s), P(256), P(512), P(1024), None, nbytes, None) == WS
+    assert lib.speckv_scores(ctypes.byref(s), P(256), P(512), P(1024), P(4096), 100, None) == WS
+    s0 = shape(n_window=0, n_lookahead=0)
+    assert lib.speckv_scores(ctypes.byref(s0), P(256), P(512), P(1024), P(4096), nbytes, None) == SHAPE
+    # nothing to score: accepted without touching the device
+    s1 = shape(n_window=1000)
+    assert lib.speckv_scores(ctypes.byref(s1), P(256), P(512), P(1024), P(4096), nbytes, None) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(C_max=-1), PARAM),
+    (dict(pool=5), PARAM),
+    (dict(pool_kernel=4), PARAM),
+    (dict(pool_kernel=0), PARAM),
+    (dict(kept=P(1026)), ALIGN),
+    (dict(pooled=P(1 << 20)), ALIAS),   # pooled overlaps scores
+    (dict(ws=None, pooled=None), WS),
+])
+def test_select_validation(lib, args, status):
+    s = shape()
+    a = dict(scores=P(1 << 20), C_max=64, pool=1, pool_kernel=7, kept=P(1 << 24), pooled=P(1 << 26), ws=P(1 << 28),
+             ws_bytes=1 << 30)
+    a.update(args)
+    assert lib.speckv_select(ctypes.byref(s), a["scores"], a["C_max"], a["pool"], a["pool_kernel"], a["kept"],
+                             a["pooled"], a["ws"], a["ws_bytes"], None) == status
+
+
+def test_compact_validation(lib):
+    s = shape()
+    k, v, kept, ko, vo, ws = P(1 << 30), P(2 << 30), P(3 << 30), P(4 << 30), P(5 << 30), P(6 << 30)
+    c = lambda *a: lib.speckv_compact(ctypes.byref(s), *a)
+    assert c(k, v, kept, 0, ko, vo, ws, 1 << 30, None) == PARAM
+    assert c(k, v, kept, 1001, ko, vo, ws, 1 << 30, None) == PARAM
+    assert c(k, v, kept, 80, k, vo, ws, 1 << 30, None) == ALIAS      # only K in place
+    assert c(k, v, kept, 80, ko, v, ws, 1 << 30, None) == ALIAS      # only V in place
+    assert c(k, k, kept, 80, ko, vo, ws, 1 << 30, None) == ALIAS     # K and V the same buffer
+    assert c(k, v, kept, 80, P((1 << 30) + 4096), vo, ws, 1 << 30, None) == ALIAS  # K out overlaps K
+    assert c(k, v, kept, 80, k, v, None, 0, None) == WS              # in place needs staging
+    assert c(k, v, kept, 80, k, v, ws, 100, None) == WS
+    assert c(P((1 << 30) + 8), v, kept, 80, ko, vo, ws, 1 << 30, None) == ALIGN
+
+
+def test_specpc_validation(lib):
+    s = shape(n_window=512, n_lookahead=1, n_in=4096)
+    f = lambda l_skip, ws=P(1 << 28), nb=1 << 30: lib.specpc_token_scores(
+        ctypes.byref(s), l_skip, P(1 << 20), P(1 << 24), None, P(1 << 26), ws, nb, None)
+    assert f(-1) == PARAM and f(2) == PARAM
+    assert f(1, None) == WS and f(1, P(1 << 28), 10) == WS
+    s0 = shape(n_window=0)
+    assert lib.specpc_token_scores(ctypes.byref(s0), 0, P(1 << 20), P(1 << 24), None, P(1 << 26), P(1 << 28),
+                                   1 << 30, None) == SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    s = shape()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        skv.speckv_scores(s, torch.zeros(4), torch.zeros(4), torch.zeros(4), None)
+
+
+def test_profile_interface_on_host(lib):
+    assert lib.speckv_profile_enable(1) == OK
+    assert lib.speckv_profile_count() == 0
+    assert lib.speckv_profile_read(0, None, None, None) == PARAM
+    assert lib.speckv_profile_enable(0) == OK
