@@ -17,6 +17,9 @@ using namespace skv;
 namespace {
 
 constexpr size_t kAlign = 256;
+// Query rows per KV head (G x observation rows): pass 1 keeps one (max, sum)
+// pair per row of a block in LDS.
+constexpr int64_t kMaxRows = 4096;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -60,8 +63,9 @@ struct ScoreWs {
   size_t part, lam, end;
 };
 ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
-  const int64_t kpb = score_keys_per_block(d.dtype, (int)d.D);
-  const int64_t chunks = (keys + kpb - 1) / kpb;
+  int32_t n_sub = 1, n_chunks = 1;
+  if (keys > 0) score_plan(d.dtype, (int)d.D, units, keys, &n_sub, &n_chunks);
+  const int64_t chunks = n_chunks;
   ScoreWs w;
   w.part = 0;
   w.lam = round_up((size_t)(units * chunks * rows) * sizeof(float2));
@@ -214,6 +218,7 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   if (!q_obs || !k || !scores) return SKV_ERR_NULL;
   const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
   if (n_obs < 1) return SKV_ERR_SHAPE;
+  if ((d.Hq / d.Hkv) * n_obs > kMaxRows) return SKV_ERR_SHAPE;
   if (!aligned(q_obs, 16) || !aligned(k, 16) || !aligned(scores, 4)) return SKV_ERR_ALIGN;
   const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
   const ScoreWs w = score_ws(d, units, G * n_obs, n_pre);
@@ -235,8 +240,7 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.rows_per_qhead = (int32_t)n_obs;
   a.n_rows = (int32_t)(G * n_obs);
   a.n_keys = (int32_t)n_pre;
-  const int kpb = score_keys_per_block(d.dtype, (int)d.D);
-  a.n_chunks = (int32_t)((n_pre + kpb - 1) / kpb);
+  score_plan(d.dtype, (int)d.D, units, n_pre, &a.n_sub, &a.n_chunks);
   a.causal = 0;
   a.pos_base = 0;
   a.c = d.scale * 1.4426950408889634f;
@@ -369,6 +373,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   if (l_skip < 0 || l_skip >= d.L) return SKV_ERR_PARAM;
   const int64_t W = d.n_window;
   if (W < 1) return SKV_ERR_SHAPE;
+  if ((d.Hq / d.Hkv) * W > kMaxRows) return SKV_ERR_SHAPE;
   if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(token_scores, 4) ||
       (query_weights && !aligned(query_weights, 4)))
     return SKV_ERR_ALIGN;
@@ -392,8 +397,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   a.rows_per_qhead = (int32_t)W;
   a.n_rows = (int32_t)(G * W);
   a.n_keys = (int32_t)d.n_in;
-  const int kpb = score_keys_per_block(d.dtype, (int)d.D);
-  a.n_chunks = (int32_t)((d.n_in + kpb - 1) / kpb);
+  score_plan(d.dtype, (int)d.D, units, d.n_in, &a.n_sub, &a.n_chunks);
   a.causal = 1;
   a.pos_base = d.n_in - W;
   a.c = d.scale * 1.4426950408889634f;

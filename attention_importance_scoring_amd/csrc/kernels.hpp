@@ -22,7 +22,8 @@ struct ScoreArgs {
   int32_t rows_per_qhead;   // SpecKV: n_window + n_lookahead; SpecPC: W
   int32_t n_rows;           // R = G * rows_per_qhead
   int32_t n_keys;           // SpecKV: n_pre; SpecPC: n_in
-  int32_t n_chunks;         // key chunks per unit (pass 1 partial count)
+  int32_t n_chunks;         // key chunks per unit (one block each; pass 1 partial count)
+  int32_t n_sub;            // groups of resident keys per chunk (score_plan)
   int32_t causal;           // SpecPC: row i sees keys j <= pos_base + i
   int64_t pos_base;         // SpecPC: n_in - W
   float c;                  // logit scale * log2(e)
@@ -31,7 +32,9 @@ struct ScoreArgs {
   float* scores;            // pass 2 output: [n_units][n_keys]
 };
 
-int score_keys_per_block(int dtype, int head_dim);
+int score_keys_per_sub(int dtype, int head_dim);
+// Splits n_keys into n_chunks blocks of n_sub key groups each.
+void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_keys, int32_t* n_sub, int32_t* n_chunks);
 hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
