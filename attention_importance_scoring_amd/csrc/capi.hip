@@ -17,9 +17,8 @@ using namespace skv;
 namespace {
 
 constexpr size_t kAlign = 256;
-// Query rows per KV head (G x observation rows): pass 1 keeps one (max, sum)
-// pair per row of a block in LDS.
-constexpr int64_t kMaxRows = 4096;
+// Query rows per KV head (G x observation rows), kept well inside int32 indexing.
+constexpr int64_t kMaxRows = 1 << 20;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -63,9 +62,9 @@ struct ScoreWs {
   size_t part, lam, end;
 };
 ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
-  int32_t n_sub = 1, n_chunks = 1;
-  if (keys > 0) score_plan(d.dtype, (int)d.D, units, keys, &n_sub, &n_chunks);
-  const int64_t chunks = n_chunks;
+  ScorePlan pl{1, 1, 32, 1, 0, 0};
+  if (keys > 0 && rows > 0) score_plan(d.dtype, (int)d.D, units, rows, keys, &pl);
+  const int64_t chunks = pl.n_chunks;
   ScoreWs w;
   w.part = 0;
   w.lam = round_up((size_t)(units * chunks * rows) * sizeof(float2));
@@ -151,10 +150,17 @@ skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_
     if (st_ != SKV_OK) return st_;    \
   } while (0)
 
-skv_status run_scoring(const Dims& d, ScoreArgs& a, hipStream_t s) {
+void apply_plan(ScoreArgs& a, const ScorePlan& pl) {
+  a.n_sub = pl.n_sub;
+  a.n_chunks = pl.n_chunks;
+  a.rows_per_part = pl.rows_per_part;
+  a.n_parts = pl.n_parts;
+}
+
+skv_status run_scoring(const Dims& d, ScoreArgs& a, const ScorePlan& pl, hipStream_t s) {
   {
     ProfScope p("score_pass1", s);
-    SKV_TRY(hip_status(launch_score_pass1(d.dtype, (int)d.D, a, s)));
+    SKV_TRY(hip_status(launch_score_pass1(d.dtype, (int)d.D, a, pl.lds_pass1, s)));
   }
   {
     ProfScope p("lse_combine", s);
@@ -240,7 +246,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.rows_per_qhead = (int32_t)n_obs;
   a.n_rows = (int32_t)(G * n_obs);
   a.n_keys = (int32_t)n_pre;
-  score_plan(d.dtype, (int)d.D, units, n_pre, &a.n_sub, &a.n_chunks);
+  ScorePlan pl;
+  score_plan(d.dtype, (int)d.D, units, G * n_obs, n_pre, &pl);
+  apply_plan(a, pl);
   a.causal = 0;
   a.pos_base = 0;
   a.c = d.scale * 1.4426950408889634f;
@@ -248,9 +256,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.part = reinterpret_cast<float2*>(base + w.part);
   a.lam = reinterpret_cast<float*>(base + w.lam);
   a.scores = scores;
-  SKV_TRY(run_scoring(d, a, s));
+  SKV_TRY(run_scoring(d, a, pl, s));
   ProfScope p("score_pass2", s);
-  return hip_status(launch_score_pass2(d.dtype, (int)d.D, a, s));
+  return hip_status(launch_score_pass2(d.dtype, (int)d.D, a, pl.lds_pass2, s));
 }
 
 skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,
@@ -397,7 +405,9 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   a.rows_per_qhead = (int32_t)W;
   a.n_rows = (int32_t)(G * W);
   a.n_keys = (int32_t)d.n_in;
-  score_plan(d.dtype, (int)d.D, units, d.n_in, &a.n_sub, &a.n_chunks);
+  ScorePlan pl;
+  score_plan(d.dtype, (int)d.D, units, G * W, d.n_in, &pl);
+  apply_plan(a, pl);
   a.causal = 1;
   a.pos_base = d.n_in - W;
   a.c = d.scale * 1.4426950408889634f;
@@ -411,7 +421,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   const int rpb = specpc_rows_per_block(d.dtype, (int)d.D);
   pa.n_rowblocks = (int32_t)((W + rpb - 1) / rpb);
   pa.inv_maps = (float)(1.0 / (double)(units * G));
-  SKV_TRY(run_scoring(d, a, s));
+  SKV_TRY(run_scoring(d, a, pl, s));
   {
     ProfScope p("specpc_pass2", s);
     SKV_TRY(hip_status(launch_specpc_pass2(d.dtype, (int)d.D, pa, s)));

@@ -24,6 +24,8 @@ struct ScoreArgs {
   int32_t n_keys;           // SpecKV: n_pre; SpecPC: n_in
   int32_t n_chunks;         // key chunks per unit (one block each; pass 1 partial count)
   int32_t n_sub;            // groups of resident keys per chunk (score_plan)
+  int32_t rows_per_part;    // query rows a block holds in LDS at a time (multiple of 32)
+  int32_t n_parts;          // ceil(n_rows / rows_per_part)
   int32_t causal;           // SpecPC: row i sees keys j <= pos_base + i
   int64_t pos_base;         // SpecPC: n_in - W
   float c;                  // logit scale * log2(e)
@@ -32,12 +34,15 @@ struct ScoreArgs {
   float* scores;            // pass 2 output: [n_units][n_keys]
 };
 
-int score_keys_per_sub(int dtype, int head_dim);
-// Splits n_keys into n_chunks blocks of n_sub key groups each.
-void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_keys, int32_t* n_sub, int32_t* n_chunks);
-hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
+// Work plan of the two scoring passes for one problem size.
+struct ScorePlan {
+  int32_t n_sub, n_chunks, rows_per_part, n_parts;
+  size_t lds_pass1, lds_pass2;  // dynamic LDS bytes per block
+};
+void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl);
+hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
-hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
 
 // SpecPC pass 2: mean over (layer, query head) of the causal probabilities,
 // weighted max over window rows, per key.

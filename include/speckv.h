@@ -98,7 +98,7 @@ skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out_n_k
  * Output : scores float [n_layers][n_kv_heads][n_pre] (raw sums; they total
  *          G * (n_window + n_lookahead) per head).
  * Requires n_window + n_lookahead >= 1 and G * (n_window + n_lookahead)
- * <= 4096; n_pre = 0 is accepted and does nothing. */
+ * <= 2^20; n_pre = 0 is accepted and does nothing. */
 skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
                          void* workspace, size_t workspace_bytes, void* stream);
 
@@ -139,7 +139,7 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
  * (1 at the end of the window, 0.1 at its far edge; 1 when W = 1).
  * Inputs : q_win [n_layers][n_q_heads][W][head_dim] (all layers, skipped
  *          ones included), k.  Output: token_scores float [n_in].
- * Requires 0 <= l_skip < n_layers, 1 <= W <= n_in and G * W <= 4096. */
+ * Requires 0 <= l_skip < n_layers, 1 <= W <= n_in and G * W <= 2^20. */
 skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,
                                const float* query_weights, float* token_scores, void* workspace,
                                size_t workspace_bytes, void* stream);
