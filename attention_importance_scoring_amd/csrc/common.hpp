@@ -73,18 +73,6 @@ struct Mfma<float> {
   }
 };
 
-// Scheduling hint for a basic block that holds N_MFMA independent MFMAs and
-// vector work: alternate one MFMA with VALU_PER vector instructions, so the
-// wave keeps the matrix core and the vector ALU busy at the same time.
-template <int N_MFMA, int VALU_PER>
-__device__ __forceinline__ void interleave_mfma_valu() {
-#pragma unroll
-  for (int i = 0; i < N_MFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);  // VALU
-  }
-}
-
 __device__ __forceinline__ int acc_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

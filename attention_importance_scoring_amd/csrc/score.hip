@@ -16,9 +16,8 @@
 // loop has no barriers: the rows are read-only in LDS, each wave keeps its own
 // row statistics (pass 1) or column sums (pass 2), and the two waves that
 // share a SIMD walk the row tiles in rotated orders so that their key reloads
-// fall at different times.  Inside a wave the loop is software-pipelined: the
-// MFMAs of tile t+1 are interleaved with the exp / sum work of tile t, so the
-// matrix core and the vector ALU run at the same time.  Pass 1 puts keys on
+// fall at different times; while one wave of a SIMD waits on its MFMAs the
+// other runs its exp / sum work.  Pass 1 puts keys on
 // the MFMA M dimension and rows on N, so each lane reduces one row in-lane;
 // pass 2 swaps the operands so that each lane owns one key column.  Every sum
 // has a fixed order (no floating-point atomics): results are run-to-run
@@ -30,24 +29,13 @@
 
 namespace skv {
 
-// Registers per lane that hold resident keys.
+// Registers per lane that hold resident keys, and the most key tiles per wave.
 #ifndef SKV_KEY_VGPRS
 #define SKV_KEY_VGPRS 64
 #endif
-// Vector instructions scheduled before the first MFMA of a step, and after each.
-#ifndef SKV_P1_VALU_LEAD
-#define SKV_P1_VALU_LEAD 24
+#ifndef SKV_MAX_KT
+#define SKV_MAX_KT 2
 #endif
-#ifndef SKV_P1_VALU_PER
-#define SKV_P1_VALU_PER 8
-#endif
-#ifndef SKV_P2_VALU_LEAD
-#define SKV_P2_VALU_LEAD 16
-#endif
-#ifndef SKV_P2_VALU_PER
-#define SKV_P2_VALU_PER 5
-#endif
-
 constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block per CU)
 constexpr int kMaxSubPerChunk = 16;          // bounds the pass-2 column-sum buffer in LDS
 
@@ -56,14 +44,13 @@ struct ScoreGeom {
   using RF = RowFrag<T, D>;
   static constexpr int kNV = RF::kNV;
   static constexpr int kKTraw = SKV_KEY_VGPRS / (4 * kNV);
-  static constexpr int kKT = kKTraw < 1 ? 1 : (kKTraw > 2 ? 2 : kKTraw);  // key tiles per wave
+  static constexpr int kKT = kKTraw < 1 ? 1 : (kKTraw > SKV_MAX_KT ? SKV_MAX_KT : kKTraw);  // key tiles per wave
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
   static constexpr int kKeysPerSub = kWaves * kKeysPerWave;  // keys resident in one block at a time
   static constexpr int kRowPitch = RF::kRowBytes + 16;       // LDS pitch, padded against bank conflicts
   static constexpr int kVecPerRow = RF::kRowBytes / 16;
-  static constexpr int kMfmas = kKT * kNV * (Elem<T>::kBytes == 4 ? 4 : 1);  // MFMAs per row tile
 };
 
 struct RowStat {
@@ -218,6 +205,29 @@ __device__ __forceinline__ RowStat pass1_stats(const f32x16 (&acc)[ScoreGeom<T, 
   return merge_stat(rs, {shfl_xor32(rs.m), shfl_xor32(rs.s)});
 }
 
+// Sum of 2^(c x - ref) over the wave's keys for the lane's row, both
+// half-waves added.  Masked entries (-inf) add 0 when ref is finite.
+template <typename T, int D>
+__device__ __forceinline__ float pass1_sum_ref(const f32x16 (&acc)[ScoreGeom<T, D>::kKT], float c, float ref) {
+  using Gm = ScoreGeom<T, D>;
+  float s4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = fast_exp2(__builtin_fmaf(acc[0][i], c, -ref));
+#pragma unroll
+  for (int kt = 0; kt < Gm::kKT; ++kt)
+#pragma unroll
+    for (int i = (kt == 0 ? 4 : 0); i < 16; ++i) s4[i & 3] += fast_exp2(__builtin_fmaf(acc[kt][i], c, -ref));
+  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  return s + shfl_xor32(s);
+}
+
+// Moves the power-of-two part of the sum into the reference: s in [0.5, 1).
+__device__ __forceinline__ RowStat renormalize(RowStat st) {
+  int e;
+  const float mant = frexpf(st.s, &e);
+  return {st.m + (float)e, mant};
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(512, 1) void score_pass1_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D>;
@@ -251,58 +261,40 @@ __global__ __launch_bounds__(512, 1) void score_pass1_kernel(ScoreArgs a) {
     stage_rows<T, D>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     __syncthreads();
 
-    u32x4 kst[Gm::kKT][Gm::kNV];
-    u32x4 qf[Gm::kNV];
-    f32x16 acc_a[Gm::kKT], acc_b[Gm::kKT];
+    u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
     load_keys<T, D>(a, unit, wave_kbase(0), kst);
-    bool mask_cur = sub_masked(0);
-    {
-      const IterPos p0 = iter_pos(0, n_tiles, rot);
-      read_q_frag<T, D>(s_q, p0.rt, lane, qf);
-      if (mask_cur)
-        pass1_mfma<T, D, true>(kst, qf, pass1_rel(a, wave_kbase(0), row0 + p0.rt * 32 + lane % 32, half), acc_a);
+    bool masked = false;
+    for (int it = 0; it < n_iter; ++it) {
+      const IterPos cu = iter_pos(it, n_tiles, rot);
+      if (cu.j == 0) {  // new sub-chunk
+        if (cu.sc > 0) load_keys<T, D>(a, unit, wave_kbase(cu.sc), kst);
+        masked = sub_masked(cu.sc);
+      }
+      u32x4 qf[Gm::kNV];
+      read_q_frag<T, D>(s_q, cu.rt, lane, qf);
+      f32x16 acc[Gm::kKT];
+      const int r = cu.rt * 32 + lane % 32;
+      if (masked)
+        pass1_mfma<T, D, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
       else
-        pass1_mfma<T, D, false>(kst, qf, 0, acc_a);
-    }
-
-    // One pipeline step: MFMAs of iteration it + 1 into acc_next, statistics of
-    // iteration it from acc_cur, folded into this wave's row statistics.
-    auto step = [&](int it, f32x16 (&acc_cur)[Gm::kKT], f32x16 (&acc_next)[Gm::kKT]) {
-      const IterPos cu = iter_pos(it, n_tiles, rot), nx = iter_pos(it + 1, n_tiles, rot);
-      bool mask_next = mask_cur;
-      if (it + 1 < n_iter && nx.j == 0) {  // next sub-chunk: new resident keys
-        load_keys<T, D>(a, unit, wave_kbase(nx.sc), kst);
-        mask_next = sub_masked(nx.sc);
-      }
-      read_q_frag<T, D>(s_q, nx.rt, lane, qf);
-      RowStat rs;
-      if (mask_cur || mask_next) {
-        pass1_mfma<T, D, true>(kst, qf, pass1_rel(a, wave_kbase(nx.sc), row0 + nx.rt * 32 + lane % 32, half),
-                               acc_next);
-        rs = pass1_stats<T, D, true>(acc_cur, c);
-        __builtin_amdgcn_sched_group_barrier(0x100, Gm::kNV, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, SKV_P1_VALU_LEAD, 0);
-        interleave_mfma_valu<Gm::kMfmas, SKV_P1_VALU_PER>();
+        pass1_mfma<T, D, false>(kst, qf, 0, acc);
+      RowStat st;
+      if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
+        st = masked ? pass1_stats<T, D, true>(acc, c) : pass1_stats<T, D, false>(acc, c);
       } else {
-        pass1_mfma<T, D, false>(kst, qf, 0, acc_next);
-        rs = pass1_stats<T, D, false>(acc_cur, c);
-        __builtin_amdgcn_sched_group_barrier(0x100, Gm::kNV, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, SKV_P1_VALU_LEAD, 0);
-        interleave_mfma_valu<Gm::kMfmas, SKV_P1_VALU_PER>();
+        // Later visits sum against the row's running reference, which after
+        // renormalization is within one of log2 of the sum so far: no per-tile
+        // max and no rescaling.  A wave falls back to the exact merge when a
+        // row has no reference yet or a tile would exceed it by 2^64.
+        const RowStat cur = ws[r];  // lanes l and l ^ 32 read the same row
+        const float add = pass1_sum_ref<T, D>(acc, c, cur.m);
+        if (__any(!(add <= 0x1p64f)))
+          st = merge_stat(cur, pass1_stats<T, D, true>(acc, c));
+        else
+          st = {cur.m, cur.s + add};
       }
-      if (lane < 32) {  // this wave's own slice: no other wave touches it
-        const int r = cu.rt * 32 + lane;
-        ws[r] = (cu.sc == 0) ? rs : merge_stat(ws[r], rs);
-      }
-      mask_cur = mask_next;
-    };
-    int it = 0;
-    for (; it + 1 < n_iter; it += 2) {
-      step(it, acc_a, acc_b);
-      step(it + 1, acc_b, acc_a);
+      if (lane < 32) ws[r] = renormalize(st);  // this wave's own slice: no other wave touches it
     }
-    if (it < n_iter) step(it, acc_a, acc_b);
-
     __syncthreads();
     for (int r = threadIdx.x; r < prow; r += Gm::kThreads) {
       RowStat m = s_ws[r];
@@ -388,50 +380,37 @@ __global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
     for (int r = threadIdx.x; r < n_tiles * 32; r += Gm::kThreads) s_lam[r] = (r < prow) ? lam_unit[row0 + r] : INFINITY;
     __syncthreads();
 
-    u32x4 kst[Gm::kKT][Gm::kNV];
-    u32x4 qf[Gm::kNV];
-    f32x16 acc_a[Gm::kKT], acc_b[Gm::kKT];
-    float lam_a[16], lam_b[16];
-    float colsum[Gm::kKT];
-#pragma unroll
-    for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
+    u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
     load_keys<T, D>(a, unit, wave_kbase(0), kst);
-    {
-      const IterPos p0 = iter_pos(0, n_tiles, rot);
-      read_q_frag<T, D>(s_q, p0.rt, lane, qf);
-      read_lam(p0.rt, lam_a);
-      pass2_mfma<T, D>(kst, qf, acc_a);
-    }
-
-    // One pipeline step: MFMAs of iteration it + 1 into acc_next, column sums
-    // of iteration it from acc_cur (its lse values already in lam_cur); the lse
-    // values of iteration it + 1 are read for the next step.
-    auto step = [&](int it, f32x16 (&acc_cur)[Gm::kKT], f32x16 (&acc_next)[Gm::kKT], float (&lam_cur)[16],
-                    float (&lam_next)[16]) {
-      const IterPos cu = iter_pos(it, n_tiles, rot), nx = iter_pos(it + 1, n_tiles, rot);
-      if (it + 1 < n_iter && nx.j == 0) load_keys<T, D>(a, unit, wave_kbase(nx.sc), kst);
-      read_q_frag<T, D>(s_q, nx.rt, lane, qf);
-      pass2_mfma<T, D>(kst, qf, acc_next);
-      // acc_cur[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
+    float colsum[Gm::kKT];
+    for (int it = 0; it < n_iter; ++it) {
+      const IterPos cu = iter_pos(it, n_tiles, rot);
+      if (cu.j == 0) {  // new sub-chunk
+        if (cu.sc > 0) load_keys<T, D>(a, unit, wave_kbase(cu.sc), kst);
+#pragma unroll
+        for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
+      }
+      float lam[16];
+      read_lam(cu.rt, lam);
+      f32x16 acc[Gm::kKT];
+      u32x4 qf[Gm::kNV];
+      read_q_frag<T, D>(s_q, cu.rt, lane, qf);
+      pass2_mfma<T, D>(kst, qf, acc);
+      // acc[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
 #pragma unroll
       for (int kt = 0; kt < Gm::kKT; ++kt) {
         float s4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s4[i] = fast_exp2(__builtin_fmaf(acc_cur[kt][i], c, -lam_cur[i]));
+        for (int i = 0; i < 4; ++i) s4[i] = fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i]));
 #pragma unroll
-        for (int i = 4; i < 16; ++i) s4[i & 3] += fast_exp2(__builtin_fmaf(acc_cur[kt][i], c, -lam_cur[i]));
+        for (int i = 4; i < 16; ++i) s4[i & 3] += fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i]));
         colsum[kt] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, Gm::kNV, 0);           // MFMA operands from LDS
-      __builtin_amdgcn_sched_group_barrier(0x002, SKV_P2_VALU_LEAD, 0);  // vector work while they arrive
-      interleave_mfma_valu<Gm::kMfmas, SKV_P2_VALU_PER>();
-      read_lam(nx.rt, lam_next);
       if (cu.j + 1 == n_tiles) {  // sub-chunk complete for this part
         const int kbase = wave_kbase(cu.sc);
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt) {
           float tot = colsum[kt] + shfl_xor32(colsum[kt]);
-          colsum[kt] = 0.f;
           if (lane < 32) {
             float* slot = cs + cu.sc * Gm::kKeysPerWave + kt * 32 + lane;  // this wave's own slots
             if (!first_part) tot = *slot + tot;
@@ -444,13 +423,7 @@ __global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
           }
         }
       }
-    };
-    int it = 0;
-    for (; it + 1 < n_iter; it += 2) {
-      step(it, acc_a, acc_b, lam_a, lam_b);
-      step(it + 1, acc_b, acc_a, lam_b, lam_a);
     }
-    if (it < n_iter) step(it, acc_a, acc_b, lam_a, lam_b);
   }
 }
 

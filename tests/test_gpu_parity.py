@@ -118,6 +118,42 @@ def test_exact_ties_take_lowest_index():
     assert oracle.select_kept(want[0, 0], 40, 16).tolist() == kept.tolist()
 
 
+# 256 units make the planner give every block several consecutive groups of
+# resident keys, so rows are revisited and pass 1 sums against its running
+# per-row reference.
+_MANY_UNITS = dict(n_layers=32, n_q_heads=8, n_kv_heads=8, n_in=8200, n_window=8, n_lookahead=8, C_max=100)
+
+
+def test_many_units_revisited_rows():
+    _full_check(wl.reduced(wl.CONFIGS[2], **_MANY_UNITS), seed=12)
+
+
+@pytest.mark.parametrize("late", [True, False], ids=["jump-up", "jump-down"])
+def test_logit_jumps_between_key_groups(late):
+    # Keys in one half of every aligned 1024-key block get a logit boost of
+    # about 75 (log2 units): rows first meet small logits and later ones
+    # beyond 2^64 of their reference (jump-up), or the reverse (jump-down).
+    cfg = wl.reduced(wl.CONFIGS[2], heavy_hitters="none", **_MANY_UNITS)
+    host = wl.speckv_inputs(cfg, 13, "cpu")
+    d, n_in = cfg.head_dim, cfg.n_in
+    u = torch.ones(d) / math.sqrt(d)
+    q = host["q_obs"].float() + 12.0 * u
+    host["q_obs"] = q.to(torch.bfloat16)
+    kb = host["k_buf"].view(cfg.n_layers, cfg.n_kv_heads, n_in, d)
+    j = torch.arange(n_in)
+    boosted = ((j // 512) % 2 == (1 if late else 0)) & (j < cfg.n_pre)
+    kb[:, :, boosted] = (kb[:, :, boosted].float() + 49.0 * u).to(torch.bfloat16)
+    host["k"] = kb
+    inp = _to(host, "cuda")
+    out = run_speckv(cfg, inp)
+    torch.cuda.synchronize()
+    want = oracle.speckv_scores(np64(host["q_obs"]), np64(host["k"]), cfg.n_window)
+    got = out["scores"].cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_scores_close(got, want, cfg.G, cfg.n_obs)
+    np.testing.assert_allclose(got.sum(-1), cfg.G * cfg.n_obs, rtol=1e-4)
+
+
 def test_in_place_equals_out_of_place_and_deterministic():
     cfg = wl.reduced(wl.CONFIGS[4], n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
     host = wl.speckv_inputs(cfg, 7, "cpu")
