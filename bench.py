@@ -13,7 +13,6 @@ and resident in HBM before timing starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,17 +25,7 @@ METRIC = "keys scored+compacted/sec and % of HBM/MFMA roofline at n_in=64K, 32B 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["attention_importance_scoring_amd/csrc/" + f for f in
-                  ("common.hpp", "kernels.hpp", "score.hip", "select.hip", "specpc.hip", "capi.hip")]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "speckv_kernels_{workload}_traffic.json")
 
 
 def parse():
@@ -99,20 +88,22 @@ def speckv_cpu_baseline(cfg, inp, budget_s=12.0):
                       f"{t_total:.1f} s of fp64 NumPy"}
 
 
-def traffic_for(kernel: str, per_launch_alg_bytes=None):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when it is absent or was taken on different kernel sources."""
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)
+    from the committed counter summary, or None when it is absent, covers
+    another workload or was taken on different kernel sources."""
+    from attention_importance_scoring_amd.counters import kernel_source_hash
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
-    k = t.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("hbm_bytes_per_launch")
+    for name, k in t.get("kernels", {}).items():
+        if name.startswith(kernel + "_kernel"):
+            return k.get("hbm_bytes_per_launch")
+    return None
 
 
 def bench_speckv(args, cfg, torch, skv, wl):
@@ -180,7 +171,7 @@ def bench_speckv(args, cfg, torch, skv, wl):
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = flops_per_launch / avg_s / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom)}
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name)}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
     path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
     out = {
@@ -264,13 +255,14 @@ def main():
     else:
         out, inp = bench_speckv(args, cfg, torch, skv, wl)
     if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        # plain streaming kernel of known size for counter calibration: M MiB read, M MiB written
+        n = (args.calib_copy_mib << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
-        out["calib_copy_bytes"] = n
+        out["calib_copy_bytes"] = n * 4
     if not args.no_cpu_baseline and args.workload != "specpc_draft_32k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = speckv_cpu_baseline(cfg, inp)
