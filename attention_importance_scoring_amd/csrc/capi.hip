@@ -59,7 +59,7 @@ skv_status check_shape(const skv_shape* s, Dims* d) {
 
 // ---- workspace layouts -------------------------------------------------
 struct ScoreWs {
-  size_t part, lam, end;
+  size_t part, lam, colpart, end;
 };
 ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
   ScorePlan pl{1, 1, 32, 1, 0, 0};
@@ -68,7 +68,8 @@ ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
   ScoreWs w;
   w.part = 0;
   w.lam = round_up((size_t)(units * chunks * rows) * sizeof(float2));
-  w.end = w.lam + round_up((size_t)(units * rows) * sizeof(float));
+  w.colpart = w.lam + round_up((size_t)(units * rows) * sizeof(float));
+  w.end = w.colpart + round_up((size_t)((pl.n_parts - 1) * units * keys) * sizeof(float));
   return w;
 }
 
@@ -255,10 +256,16 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   char* base = static_cast<char*>(ws);
   a.part = reinterpret_cast<float2*>(base + w.part);
   a.lam = reinterpret_cast<float*>(base + w.lam);
+  a.colpart = reinterpret_cast<float*>(base + w.colpart);
   a.scores = scores;
   SKV_TRY(run_scoring(d, a, pl, s));
-  ProfScope p("score_pass2", s);
-  return hip_status(launch_score_pass2(d.dtype, (int)d.D, a, pl.lds_pass2, s));
+  {
+    ProfScope p("score_pass2", s);
+    SKV_TRY(hip_status(launch_score_pass2(d.dtype, (int)d.D, a, pl.lds_pass2, s)));
+  }
+  if (a.n_parts == 1) return SKV_OK;
+  ProfScope p("colsum_combine", s);
+  return hip_status(launch_colsum_combine(a, s));
 }
 
 skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,
@@ -415,6 +422,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   a.part = reinterpret_cast<float2*>(base + w.sc.part);
   a.lam = reinterpret_cast<float*>(base + w.sc.lam);
   a.scores = nullptr;
+  a.colpart = nullptr;
   pa.weights = query_weights;
   pa.rowblock_max = reinterpret_cast<float*>(base + w.rowmax);
   pa.token_scores = token_scores;

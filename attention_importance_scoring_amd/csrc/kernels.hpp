@@ -22,16 +22,17 @@ struct ScoreArgs {
   int32_t rows_per_qhead;   // SpecKV: n_window + n_lookahead; SpecPC: W
   int32_t n_rows;           // R = G * rows_per_qhead
   int32_t n_keys;           // SpecKV: n_pre; SpecPC: n_in
-  int32_t n_chunks;         // key chunks per unit (one block each; pass 1 partial count)
+  int32_t n_chunks;         // key chunks per unit (pass 1 partial count)
   int32_t n_sub;            // groups of resident keys per chunk (score_plan)
-  int32_t rows_per_part;    // query rows a block holds in LDS at a time (multiple of 32)
-  int32_t n_parts;          // ceil(n_rows / rows_per_part)
+  int32_t rows_per_part;    // query rows a block holds in LDS (multiple of 32)
+  int32_t n_parts;          // ceil(n_rows / rows_per_part); one block per (unit, chunk, part)
   int32_t causal;           // SpecPC: row i sees keys j <= pos_base + i
   int64_t pos_base;         // SpecPC: n_in - W
   float c;                  // logit scale * log2(e)
   float2* part;             // pass 1 output: [n_units][n_chunks][R] (max, sum) in log2 units
   float* lam;               // combine output / pass 2 input: [n_units][R] log2-domain lse
   float* scores;            // pass 2 output: [n_units][n_keys]
+  float* colpart;           // pass 2, parts 1 ..: [n_parts - 1][n_units][n_keys] column sums
 };
 
 // Work plan of the two scoring passes for one problem size.
@@ -43,6 +44,7 @@ void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_
 hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
+hipError_t launch_colsum_combine(const ScoreArgs& a, hipStream_t s);  // when n_parts > 1
 
 // SpecPC pass 2: mean over (layer, query head) of the causal probabilities,
 // weighted max over window rows, per key.

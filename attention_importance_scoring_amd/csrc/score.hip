@@ -9,15 +9,17 @@
 // stored.  Pass 2 (column sums): score_j = sum_r 2^(c * <q_r, k_j> - lse_r).
 //
 // Work split: one 8-wave block per CU owns a chunk of consecutive keys of one
-// unit (layer, KV head).  It copies a "part" of the unit's query rows (as many
-// 32-row tiles as fit in LDS, up to ~150 KB) into LDS once; then every wave
-// walks its share of the chunk, kKT tiles of 32 keys at a time held in
-// registers as an MFMA operand, against every row tile of the part.  The main
-// loop has no barriers: the rows are read-only in LDS, each wave keeps its own
-// row statistics (pass 1) or column sums (pass 2), and the two waves that
-// share a SIMD walk the row tiles in rotated orders so that their key reloads
-// fall at different times; while one wave of a SIMD waits on its MFMAs the
-// other runs its exp / sum work.  Pass 1 puts keys on
+// unit (layer, KV head) and one "part" of the unit's query rows: as many
+// 32-row tiles as fit in LDS (up to ~150 KB), copied there once.  The parts
+// of a chunk are neighbouring blocks on one XCD, so K comes from HBM about
+// once and from L2 for the other parts; pass 2 writes one column-sum row per
+// part and a small kernel adds them in part order.  Every wave walks its
+// share of the chunk, kKT tiles of 32 keys at a time held in registers as an
+// MFMA operand, against every row tile of the part.  The main loop has no
+// barriers: the rows are read-only in LDS, each wave keeps its own row
+// statistics (pass 1) or column sums (pass 2), and the waves that share a
+// SIMD walk the row tiles in rotated orders, so that while one waits on its
+// MFMAs another runs its exp / sum work.  Pass 1 puts keys on
 // the MFMA M dimension and rows on N, so each lane reduces one row in-lane;
 // pass 2 swaps the operands so that each lane owns one key column.  Every sum
 // has a fixed order (no floating-point atomics): results are run-to-run
@@ -36,8 +38,12 @@ namespace skv {
 #ifndef SKV_MAX_KT
 #define SKV_MAX_KT 2
 #endif
+// Waves per block (one block per CU): 4 SIMDs x SKV_WAVES / 4 waves each.
+#ifndef SKV_WAVES
+#define SKV_WAVES 8
+#endif
 constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block per CU)
-constexpr int kMaxSubPerChunk = 16;          // bounds the pass-2 column-sum buffer in LDS
+constexpr int kMaxSubPerChunk = 16;          // groups of resident keys per block
 
 template <typename T, int D>
 struct ScoreGeom {
@@ -45,7 +51,7 @@ struct ScoreGeom {
   static constexpr int kNV = RF::kNV;
   static constexpr int kKTraw = SKV_KEY_VGPRS / (4 * kNV);
   static constexpr int kKT = kKTraw < 1 ? 1 : (kKTraw > SKV_MAX_KT ? SKV_MAX_KT : kKTraw);  // key tiles per wave
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = SKV_WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
   static constexpr int kKeysPerSub = kWaves * kKeysPerWave;  // keys resident in one block at a time
@@ -157,6 +163,19 @@ __device__ __forceinline__ int pass1_rel(const ScoreArgs& a, int kbase, int row,
   return (int)(rel < -4096 ? -4096 : (rel > 4096 ? 4096 : rel));
 }
 
+// Block -> (unit, key chunk, row part).  The parts of one chunk are adjacent
+// logical blocks, which the XCD-contiguous remap puts on the same XCD at about
+// the same time, so the keys the first part reads from HBM reach the others
+// from that XCD's L2.
+struct BlockPos {
+  int unit, chunk, part;
+};
+__device__ __forceinline__ BlockPos block_pos(const ScoreArgs& a) {
+  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int part = logical % a.n_parts, uc = logical / a.n_parts;
+  return {uc / a.n_chunks, uc % a.n_chunks, part};
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1
 
@@ -229,14 +248,14 @@ __device__ __forceinline__ RowStat renormalize(RowStat st) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void score_pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass1_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                      // [rows_per_part][pitch]
   RowStat* s_ws = reinterpret_cast<RowStat*>(smem + (size_t)a.rows_per_part * Gm::kRowPitch);  // [waves][rows_per_part]
 
-  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int unit = logical / a.n_chunks, chunk = logical % a.n_chunks;
+  const BlockPos bp = block_pos(a);
+  const int unit = bp.unit, chunk = bp.chunk;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, half = lane / 32;
   const int key0 = chunk * a.n_sub * Gm::kKeysPerSub;
   const int n_sub = min(a.n_sub, (a.n_keys - key0 + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub);
@@ -251,13 +270,12 @@ __global__ __launch_bounds__(512, 1) void score_pass1_kernel(ScoreArgs a) {
     return (kb + Gm::kKeysPerWave > a.n_keys) || (a.causal && (int64_t)kb + Gm::kKeysPerWave - 1 > a.pos_base);
   };
 
-  for (int p = 0; p < a.n_parts; ++p) {
-    const int row0 = p * a.rows_per_part;
+  {
+    const int row0 = bp.part * a.rows_per_part;
     const int prow = min(a.rows_per_part, a.n_rows - row0);
     const int n_tiles = (prow + 31) / 32;
-    const int rot = (wave >= 4) ? n_tiles / 2 : 0;
+    const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
     const int n_iter = n_sub * n_tiles;
-    __syncthreads();  // the previous part's rows and statistics are no longer in use
     stage_rows<T, D>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     __syncthreads();
 
@@ -320,6 +338,16 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreArgs a) {
   a.lam[idx] = M + log2f(S);
 }
 
+// scores += column sums of parts 1 .. n_parts - 1, in part order.
+__global__ __launch_bounds__(256) void colsum_combine_kernel(ScoreArgs a) {
+  const int64_t n = (int64_t)a.n_units * a.n_keys;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  float v = a.scores[idx];
+  for (int p = 1; p < a.n_parts; ++p) v += a.colpart[(int64_t)(p - 1) * n + idx];
+  a.scores[idx] = v;
+}
+
 // ---------------------------------------------------------------------------
 // Pass 2
 
@@ -337,23 +365,23 @@ __device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D>::k
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                    // [rows_per_part][pitch]
   float* s_lam = reinterpret_cast<float*>(smem + (size_t)a.rows_per_part * Gm::kRowPitch);  // [rows_per_part]
-  float* s_cs = s_lam + a.rows_per_part;  // [waves][n_sub][keys per wave]: sums of earlier parts
 
-  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int unit = logical / a.n_chunks, chunk = logical % a.n_chunks;
+  const BlockPos bp = block_pos(a);
+  const int unit = bp.unit, chunk = bp.chunk;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, half = lane / 32;
   const int key0 = chunk * a.n_sub * Gm::kKeysPerSub;
   const int n_sub = min(a.n_sub, (a.n_keys - key0 + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub);
   const float c = a.c;
   const char* qrows = unit_rows<T>(a, unit);
   const float* lam_unit = a.lam + (int64_t)unit * a.n_rows;
-  float* out = a.scores + (int64_t)unit * a.n_keys;
-  float* cs = s_cs + wave * a.n_sub * Gm::kKeysPerWave;
+  // part 0 writes the scores, part p > 0 its own partial column sums
+  float* out = (bp.part == 0 ? a.scores : a.colpart + (int64_t)(bp.part - 1) * a.n_units * a.n_keys) +
+               (int64_t)unit * a.n_keys;
   auto wave_kbase = [&](int sc) { return key0 + sc * Gm::kKeysPerSub + wave * Gm::kKeysPerWave; };
   // lse of row tile rt's rows m(i) = acc_row(i, half), for the lane's half-wave.
   auto read_lam = [&](int rt, float (&lam)[16]) {
@@ -368,14 +396,12 @@ __global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
     }
   };
 
-  for (int p = 0; p < a.n_parts; ++p) {
-    const int row0 = p * a.rows_per_part;
+  {
+    const int row0 = bp.part * a.rows_per_part;
     const int prow = min(a.rows_per_part, a.n_rows - row0);
     const int n_tiles = (prow + 31) / 32;
-    const int rot = (wave >= 4) ? n_tiles / 2 : 0;
+    const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
     const int n_iter = n_sub * n_tiles;
-    const bool first_part = (p == 0), last_part = (p + 1 == a.n_parts);
-    __syncthreads();  // the previous part's rows are no longer in use
     stage_rows<T, D>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     for (int r = threadIdx.x; r < n_tiles * 32; r += Gm::kThreads) s_lam[r] = (r < prow) ? lam_unit[row0 + r] : INFINITY;
     __syncthreads();
@@ -410,17 +436,9 @@ __global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
         const int kbase = wave_kbase(cu.sc);
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt) {
-          float tot = colsum[kt] + shfl_xor32(colsum[kt]);
-          if (lane < 32) {
-            float* slot = cs + cu.sc * Gm::kKeysPerWave + kt * 32 + lane;  // this wave's own slots
-            if (!first_part) tot = *slot + tot;
-            if (last_part) {
-              const int key = kbase + kt * 32 + lane;
-              if (key < a.n_keys) out[key] = tot;
-            } else {
-              *slot = tot;
-            }
-          }
+          const float tot = colsum[kt] + shfl_xor32(colsum[kt]);
+          const int key = kbase + kt * 32 + lane;
+          if (lane < 32 && key < a.n_keys) out[key] = tot;
         }
       }
     }
@@ -432,22 +450,12 @@ __global__ __launch_bounds__(512, 1) void score_pass2_kernel(ScoreArgs a) {
 template <typename T, int D>
 static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   using Gm = ScoreGeom<T, D>;
-  // Key chunks: enough blocks for several rounds over 256 CUs (one block per CU).
-  constexpr int64_t kTargetBlocks = 2048;
-  const int64_t subs = (n_keys + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub;
-  int64_t chunks = (kTargetBlocks + n_units - 1) / n_units;
-  chunks = chunks < 1 ? 1 : (chunks > subs ? subs : chunks);
-  int64_t per = (subs + chunks - 1) / chunks;
-  if (per > kMaxSubPerChunk) per = kMaxSubPerChunk;
-  pl->n_sub = (int32_t)per;
-  pl->n_chunks = (int32_t)((subs + per - 1) / per);
-  // Row parts: as many 32-row tiles as the LDS budget holds.
+  // Row parts: as many 32-row tiles as the LDS budget holds, split evenly.
   const int64_t tiles = (n_rows + 31) / 32;
   const int64_t per_row1 = Gm::kRowPitch + (int64_t)Gm::kWaves * (int64_t)sizeof(RowStat);
-  const int64_t cs_bytes = (int64_t)Gm::kWaves * per * Gm::kKeysPerWave * 4;
   const int64_t per_row2 = Gm::kRowPitch + 4;
   int64_t fit = kScoreLdsBudget / (32 * per_row1);
-  const int64_t fit2 = (kScoreLdsBudget - cs_bytes) / (32 * per_row2);
+  const int64_t fit2 = kScoreLdsBudget / (32 * per_row2);
   fit = fit < fit2 ? fit : fit2;
   if (fit < 1) fit = 1;
   const int64_t parts = (tiles + fit - 1) / fit;
@@ -455,7 +463,19 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
   pl->rows_per_part = (int32_t)(tpp * 32);
   pl->n_parts = (int32_t)((tiles + tpp - 1) / tpp);
   pl->lds_pass1 = (size_t)(pl->rows_per_part * per_row1);
-  pl->lds_pass2 = (size_t)(pl->rows_per_part * per_row2 + cs_bytes);
+  pl->lds_pass2 = (size_t)(pl->rows_per_part * per_row2);
+  // Key chunks: enough blocks (units x chunks x parts) for several rounds over
+  // the 256 CUs, one block per CU; at most kMaxSubPerChunk groups of resident
+  // keys per block, so the parts of a chunk stay close together in time.
+  constexpr int64_t kTargetBlocks = 2048;
+  const int64_t subs = (n_keys + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub;
+  const int64_t ups = n_units * pl->n_parts;
+  int64_t chunks = (kTargetBlocks + ups - 1) / ups;
+  chunks = chunks < 1 ? 1 : (chunks > subs ? subs : chunks);
+  int64_t per = (subs + chunks - 1) / chunks;
+  if (per > kMaxSubPerChunk) per = kMaxSubPerChunk;
+  pl->n_sub = (int32_t)per;
+  pl->n_chunks = (int32_t)((subs + per - 1) / per);
 }
 
 void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
@@ -478,7 +498,7 @@ template <typename T, int D>
 static hipError_t launch_p1(const ScoreArgs& a, size_t lds, hipStream_t s) {
   hipError_t e = allow_lds(score_pass1_kernel<T, D>, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks)), block(ScoreGeom<T, D>::kThreads);
+  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D>::kThreads);
   score_pass1_kernel<T, D><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
@@ -487,7 +507,7 @@ template <typename T, int D>
 static hipError_t launch_p2(const ScoreArgs& a, size_t lds, hipStream_t s) {
   hipError_t e = allow_lds(score_pass2_kernel<T, D>, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks)), block(ScoreGeom<T, D>::kThreads);
+  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D>::kThreads);
   score_pass2_kernel<T, D><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
@@ -500,6 +520,12 @@ hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, size_
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_units * a.n_rows;
   lse_combine_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_combine(const ScoreArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_units * a.n_keys;
+  colsum_combine_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
