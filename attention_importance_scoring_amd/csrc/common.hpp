@@ -79,7 +79,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-__device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Value held by lane l ^ 32 (the other half-wave), without a trip through
+// LDS: v_permlane32_swap of v with itself gives r[0] = (v[0..31], v[0..31])
+// and r[1] = (v[32..63], v[32..63]) over lanes (0..31, 32..63).
+__device__ __forceinline__ float shfl_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // Order-preserving map of an fp32 bit pattern to uint32 (-0 is folded to +0).
 __device__ __forceinline__ uint32_t ordered_key(float f) {
