@@ -3,15 +3,21 @@
 // pairs plus the window pairs; section "Loss / training strategy", local
 // pooling keeps the kept tokens contiguous).
 //
-// One 1024-thread block per unit (layer, KV head):
+// One 1024-thread block per unit (layer, KV head), working on the
+// order-preserving uint32 image of the fp32 pooled values.  For n_pre up to
+// 64K the keys stay in registers: wave w owns the contiguous index span
+// [w S, (w + 1) S), lane l step i holds index w S + 64 i + l.
 //   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r;
-//   2. radix select, four 8-bit digits from the most significant, on the
-//      order-preserving uint32 image of the fp32 pooled values, finds the
-//      n_top-th largest value T and how many keys equal to T are taken;
-//   3. one ascending sweep emits keys with value > T, and the lowest-index
-//      keys equal to T, in index order (ballot prefix sums), so the kept
-//      list comes out sorted; the window keys are appended after them.
-// Integer decisions only: bit-exact and run-to-run deterministic.
+//   2. the n_top-th largest key T is found bit by bit from the top
+//      (T | bit is kept when at least n_top keys are >= it), each count a
+//      ballot / popcount per wave and one sum over the 16 waves;
+//   3. keys > T are all taken, and of the keys equal to T the lowest-index
+//      k_rem ones; wave-level counts and two scans over the waves give each
+//      wave its output offset, so one in-order sweep writes the kept list
+//      ascending; the window keys are appended after it.
+// Longer units use the same rule with an LDS-histogram radix select and a
+// tile-by-tile block scan.  Integer decisions only: bit-exact and run-to-run
+// deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -120,8 +126,150 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
 }
 
+// Pooled value at j (pool 0: none, 1: max, 2: in-range mean; radius r).
+// Max pooling reads clamped neighbours: a truncated window only repeats
+// in-range values, which leaves the max unchanged, and the loads carry no
+// branches.
+template <int R>  // compile-time max-pool radius, or -1 for a run-time one
+__device__ __forceinline__ float pooled_at(const float* sc, int j, int n, int pool, int r) {
+  if (pool == 1) {
+    float v = sc[j];
+    if constexpr (R >= 0) {
+#pragma unroll
+      for (int o = 1; o <= R; ++o) v = fmaxf(v, fmaxf(sc[max(j - o, 0)], sc[min(j + o, n - 1)]));
+    } else {
+      for (int o = 1; o <= r; ++o) v = fmaxf(v, fmaxf(sc[max(j - o, 0)], sc[min(j + o, n - 1)]));
+    }
+    return v;
+  }
+  if (pool == 2 && r > 0) {
+    const int lo = j - r < 0 ? 0 : j - r, hi = j + r >= n ? n - 1 : j + r;
+    float s = 0.f;
+    for (int t = lo; t <= hi; ++t) s += sc[t];
+    return s / (float)(hi - lo + 1);
+  }
+  return sc[j];
+}
+
+// Sum of one value per wave over the block's 16 waves (every thread gets it).
+// Also returns the sum over the waves before this one.
+__device__ __forceinline__ uint32_t waves_sum(uint32_t v, uint32_t* s_red, uint32_t& before) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  uint32_t tot = 0, pre = 0;
+#pragma unroll
+  for (int w4 = 0; w4 < kSelWaves / 4; ++w4) {
+    const u32x4 t4 = reinterpret_cast<const u32x4*>(s_red)[w4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pre += (4 * w4 + q < wave) ? t4[q] : 0u;
+      tot += t4[q];
+    }
+  }
+  __syncthreads();
+  before = pre;
+  return tot;
+}
+
+// Sum over the wave of a per-lane count below 128, as seven ballots over
+// its bits (the result is wave-uniform).
+__device__ __forceinline__ uint32_t wave_count(uint32_t c) {
+  uint32_t t = 0u;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) t += (uint32_t)__popcll(__ballot((c >> b) & 1u)) << b;
+  return t;
+}
+
+template <int E, int R>  // keys per lane held in registers (n_pre <= 16 * 64 * E); max-pool radius or -1
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_red[kSelWaves];
+  const int unit = blockIdx.x;
+  const int n = a.n_pre, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const float* sc = a.scores + (int64_t)unit * n;
+  float* pl = a.pooled + (int64_t)unit * n;
+  int32_t* kept = a.kept + (int64_t)unit * (a.n_top + a.n_window);
+  const int span = (n + kSelWaves * kWave - 1) / (kSelWaves * kWave) * kWave;  // indices per wave
+  const int base = wave * span;
+
+  for (int t = tid; t < a.n_window; t += kSelThreads) kept[a.n_top + t] = n + t;
+  // 1. pooling, then this lane's pooled values (which it wrote itself) as
+  // keys; key 0 marks padding (every non-negative score maps above 2^31)
+#pragma unroll 8
+  for (int i = 0; i < E; ++i) {
+    const int j = base + i * kWave + lane;
+    if (i * kWave < span && j < n) pl[j] = pooled_at<R>(sc, j, n, a.pool, a.pool_radius);
+  }
+  __syncthreads();  // the block's pooled values are visible to all its threads
+  uint32_t key[E];
+  const float* pl_lane = pl + base + lane;
+  const int lim = min(span, n - base) - lane;  // this lane's steps i hold an index iff i * 64 < lim
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float v = pl_lane[min(i * kWave, n - 1 - base - lane)];  // clamped: no branch, padding dropped
+    key[i] = (i * kWave < lim) ? ordered_key(v) : 0u;
+  }
+  if (a.n_top >= n) {
+    for (int j = tid; j < n; j += kSelThreads) kept[j] = j;
+    return;
+  }
+  if (a.n_top == 0) return;
+  const uint32_t n_top = (uint32_t)a.n_top;
+
+  // 2. T = the n_top-th largest key
+  uint32_t T = 0u, before;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int i = 0; i < E; ++i) c += key[i] >= cand ? 1u : 0u;
+    if (waves_sum(wave_count(c), s_red, before) >= n_top) T = cand;
+  }
+
+  // 3. ascending emission
+  uint32_t gt_l = 0u, eq_l = 0u;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    gt_l += key[i] > T ? 1u : 0u;
+    eq_l += key[i] == T ? 1u : 0u;
+  }
+  const uint32_t gt = wave_count(gt_l), eq = wave_count(eq_l);
+  uint32_t gt_before, eq_before;
+  const uint32_t k_rem = n_top - waves_sum(gt, s_red, gt_before);  // keys equal to T to take
+  waves_sum(eq, s_red, eq_before);
+  const uint32_t eq_take = eq_before >= k_rem ? 0u : (k_rem - eq_before < eq ? k_rem - eq_before : eq);
+  uint32_t run_sel;
+  waves_sum(gt + eq_take, s_red, run_sel);
+  uint32_t run_eq = eq_before;
+  const uint64_t lower = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const uint64_t m_eq = __ballot(key[i] == T);
+    const bool is_eq = key[i] == T;
+    const bool take = key[i] > T || (is_eq && run_eq + (uint32_t)__popcll(m_eq & lower) < k_rem);
+    const uint64_t m_take = __ballot(take);
+    if (take) kept[run_sel + (uint32_t)__popcll(m_take & lower)] = base + i * kWave + lane;
+    run_eq += (uint32_t)__popcll(m_eq);
+    run_sel += (uint32_t)__popcll(m_take);
+  }
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  select_kernel<<<dim3((unsigned)a.n_units), dim3(kSelThreads), 0, s>>>(a);
+  const dim3 grid((unsigned)a.n_units), block(kSelThreads);
+  const int64_t per_lane = ((int64_t)a.n_pre + kSelThreads - 1) / kSelThreads;
+  const bool r3 = a.pool == 1 && a.pool_radius == 3;  // the width-7 max pool
+  if (per_lane <= 4) {
+    if (r3) select_reg_kernel<4, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<4, -1><<<grid, block, 0, s>>>(a);
+  } else if (per_lane <= 16) {
+    if (r3) select_reg_kernel<16, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<16, -1><<<grid, block, 0, s>>>(a);
+  } else if (per_lane <= 32) {
+    if (r3) select_reg_kernel<32, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<32, -1><<<grid, block, 0, s>>>(a);
+  } else if (per_lane <= 64) {
+    if (r3) select_reg_kernel<64, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<64, -1><<<grid, block, 0, s>>>(a);
+  } else {
+    select_kernel<<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
