@@ -211,7 +211,8 @@ skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t*
   const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
   const int64_t n_pre = d.n_in - d.n_window;
   size_t need = score_ws(d, units, G * (d.n_window + d.n_lookahead), n_pre).end;           // speckv_scores
-  need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)));                  // speckv_select
+  need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)) +                   // speckv_select
+                            select_candidate_bytes(units, n_pre, keep_count(d, C_max) - d.n_window));
   need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
   if (d.n_window >= 1) need = std::max(need, specpc_ws(d, units).end);                         // specpc_token_scores
   *out = need;
@@ -282,21 +283,33 @@ skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_
   if (pooled && ranges_overlap(pooled, (size_t)(units * n_pre) * 4, scores, (size_t)(units * n_pre) * 4))
     return SKV_ERR_ALIAS;
   if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, scores, (size_t)(units * n_pre) * 4)) return SKV_ERR_ALIAS;
+  const int64_t n_top = n_keep - d.n_window;
+  const int n_seg = select_segments(units, n_pre, n_top);
+  const size_t pool_bytes = pooled ? 0 : round_up((size_t)(units * n_pre) * sizeof(float));
+  const size_t cand_bytes = select_candidate_bytes(units, n_pre, n_top);
   float* pl = pooled;
-  if (!pl) {
-    if (!ws || ws_bytes < (size_t)(units * n_pre) * sizeof(float)) return SKV_ERR_WORKSPACE;
-    if (!aligned(ws, 4)) return SKV_ERR_ALIGN;
-    pl = static_cast<float*>(ws);
+  char* cand = nullptr;
+  if (pool_bytes + cand_bytes > 0) {
+    if (!ws || ws_bytes < pool_bytes + cand_bytes) return SKV_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+    if (!pooled) pl = static_cast<float*>(ws);
+    cand = static_cast<char*>(ws) + pool_bytes;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   SelectArgs a{};
+  a.n_seg = n_seg;
+  a.seg_len = (int32_t)((n_pre + n_seg - 1) / n_seg);
+  if (n_seg > 1) {
+    a.cand_key = reinterpret_cast<uint32_t*>(cand);
+    a.cand_idx = reinterpret_cast<int32_t*>(cand + (size_t)(units * n_seg * n_top) * 4);
+  }
   a.scores = scores;
   a.pooled = pl;
   a.kept = kept;
   a.n_units = (int32_t)units;
   a.n_pre = (int32_t)n_pre;
   a.n_window = (int32_t)d.n_window;
-  a.n_top = (int32_t)(n_keep - d.n_window);
+  a.n_top = (int32_t)n_top;
   a.pool = pool;
   a.pool_radius = pool == SKV_POOL_NONE ? 0 : pool_kernel / 2;
   ProfScope p("select", s);

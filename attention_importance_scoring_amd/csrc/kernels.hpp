@@ -72,7 +72,17 @@ struct SelectArgs {
   int32_t n_top;            // min(C_max, n_pre)
   int32_t pool;             // skv_pool
   int32_t pool_radius;      // pool_kernel / 2
+  // Two-stage form for long units with few heads: n_seg segments of seg_len
+  // keys each keep their local top n_top as (key, index) candidates in
+  // [n_units][n_seg][n_top] (workspace); a second kernel selects among them.
+  int32_t n_seg;
+  int32_t seg_len;
+  uint32_t* cand_key;
+  int32_t* cand_idx;
 };
+// Segments per unit for the two-stage form (1: single stage) and its workspace bytes.
+int select_segments(int64_t n_units, int64_t n_pre, int64_t n_top);
+size_t select_candidate_bytes(int64_t n_units, int64_t n_pre, int64_t n_top);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
 // Row gather: dst[u][t] = src[u][idx[u][t]] (or src[u][t] when idx is null).

@@ -5,21 +5,25 @@
 //
 // One 1024-thread block per unit (layer, KV head), working on the
 // order-preserving uint32 image of the fp32 pooled values.  For n_pre up to
-// 64K the keys stay in registers: wave w owns the contiguous index span
-// [w S, (w + 1) S), lane l step i holds index w S + 64 i + l.
+// 64K the keys stay in registers: wave w owns a contiguous index span, lane l
+// step i holds index w S + 64 i + l.
 //   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r;
 //   2. the n_top-th largest key T is found bit by bit from the top
 //      (T | bit is kept when at least n_top keys are >= it), each count a
-//      ballot / popcount per wave and one sum over the 16 waves;
+//      per-lane sum, seven ballots and one sum over the 16 waves;
 //   3. keys > T are all taken, and of the keys equal to T the lowest-index
-//      k_rem ones; wave-level counts and two scans over the waves give each
-//      wave its output offset, so one in-order sweep writes the kept list
+//      k_rem ones; wave-level counts and scans over the waves give each wave
+//      its output offset, so one in-order sweep writes the kept list
 //      ascending; the window keys are appended after it.
-// Longer units use the same rule with an LDS-histogram radix select and a
-// tile-by-tile block scan.  Integer decisions only: bit-exact and run-to-run
-// deterministic.
+// Units that are long for their number (few heads, long context) run in two
+// stages: segments keep their own top n_top as candidates, then one block per
+// unit applies the same rule to the candidates.  Longer units still use an
+// LDS-histogram radix select with a tile-by-tile block scan.  Integer
+// decisions only: bit-exact and run-to-run deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
+
+#include <math.h>
 
 namespace skv {
 
@@ -181,41 +185,91 @@ __device__ __forceinline__ uint32_t wave_count(uint32_t c) {
   return t;
 }
 
-template <int E, int R>  // keys per lane held in registers (n_pre <= 16 * 64 * E); max-pool radius or -1
+enum SelMode { kSelDirect = 0, kSelSegment = 1, kSelMerge = 2 };
+
+// Selection with the keys of one block in registers (up to 64 per lane).
+//   direct : block = unit; keys = pooled scores; writes the kept list.
+//   segment: block = (unit, segment); keys = pooled scores of the segment;
+//            writes the segment's own top n_top as (key, index) candidates.
+//   merge  : block = unit; keys = the segments' candidates in segment order
+//            (so in index order); writes the kept list.
+// The unit's top n_top is contained in the union of the segments' own top
+// n_top (lowest indices first on ties in both), so the merge is exact.
+template <int E, int R, int MODE>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_red[kSelWaves];
-  const int unit = blockIdx.x;
-  const int n = a.n_pre, tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = a.n_pre;
+  int unit = blockIdx.x, s0 = 0, len = n, n_top = a.n_top;
+  if (MODE == kSelSegment) {
+    unit = blockIdx.x / a.n_seg;
+    s0 = (blockIdx.x % a.n_seg) * a.seg_len;
+    len = min(a.seg_len, n - s0);
+    n_top = min(a.n_top, len);
+  } else if (MODE == kSelMerge) {
+    len = a.n_seg * a.n_top;
+  }
   const float* sc = a.scores + (int64_t)unit * n;
   float* pl = a.pooled + (int64_t)unit * n;
   int32_t* kept = a.kept + (int64_t)unit * (a.n_top + a.n_window);
-  const int span = (n + kSelWaves * kWave - 1) / (kSelWaves * kWave) * kWave;  // indices per wave
+  const int64_t cbase = (int64_t)unit * a.n_seg * a.n_top + (MODE == kSelSegment ? (int64_t)(blockIdx.x % a.n_seg) * a.n_top : 0);
+  uint32_t* cand_key = a.cand_key + cbase;
+  int32_t* cand_idx = a.cand_idx + cbase;
+  const int span = (len + kSelThreads - 1) / kSelThreads * kWave;  // positions per wave (contiguous)
   const int base = wave * span;
+  const int lim = min(span, len - base) - lane;  // this lane's step i holds a position iff i * 64 < lim
 
-  for (int t = tid; t < a.n_window; t += kSelThreads) kept[a.n_top + t] = n + t;
-  // 1. pooling, then this lane's pooled values (which it wrote itself) as
-  // keys; key 0 marks padding (every non-negative score maps above 2^31)
-#pragma unroll 8
-  for (int i = 0; i < E; ++i) {
-    const int j = base + i * kWave + lane;
-    if (i * kWave < span && j < n) pl[j] = pooled_at<R>(sc, j, n, a.pool, a.pool_radius);
-  }
-  __syncthreads();  // the block's pooled values are visible to all its threads
+  if (MODE != kSelSegment)
+    for (int t = tid; t < a.n_window; t += kSelThreads) kept[a.n_top + t] = n + t;
+
+  // 1. keys; key 0 marks padding (every non-negative score maps above 2^31)
   uint32_t key[E];
-  const float* pl_lane = pl + base + lane;
-  const int lim = min(span, n - base) - lane;  // this lane's steps i hold an index iff i * 64 < lim
+  if constexpr (MODE == kSelMerge) {
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const float v = pl_lane[min(i * kWave, n - 1 - base - lane)];  // clamped: no branch, padding dropped
-    key[i] = (i * kWave < lim) ? ordered_key(v) : 0u;
+    for (int i = 0; i < E; ++i) {
+      const int p = base + i * kWave + lane;
+      const int pc = min(p, len - 1);
+      const int seg = pc / a.n_top;
+      const int seg_keep = min(a.n_top, min(a.seg_len, n - seg * a.seg_len));
+      const uint32_t k = cand_key[pc];
+      key[i] = (i * kWave < lim && pc - seg * a.n_top < seg_keep) ? k : 0u;
+    }
+  } else {
+#pragma unroll 8
+    for (int i = 0; i < E; ++i) {
+      const int p = base + i * kWave + lane;
+      if (i * kWave < lim) pl[s0 + p] = pooled_at<R>(sc, s0 + p, n, a.pool, a.pool_radius);
+    }
+    __syncthreads();  // the block's pooled values are visible to all its threads
+    const float* pl_lane = pl + s0 + base + lane;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float v = pl_lane[min(i * kWave, len - 1 - base - lane)];  // clamped: no branch, padding dropped
+      key[i] = (i * kWave < lim) ? ordered_key(v) : 0u;
+    }
   }
-  if (a.n_top >= n) {
-    for (int j = tid; j < n; j += kSelThreads) kept[j] = j;
+  // Index (in the unit) of the element at step i of this lane.
+  auto index_of = [&](int i) -> int {
+    const int p = base + i * kWave + lane;
+    if constexpr (MODE == kSelMerge) return cand_idx[p];
+    return s0 + p;
+  };
+  auto emit = [&](uint32_t pos, int i) {
+    if constexpr (MODE == kSelSegment) {
+      cand_key[pos] = key[i];
+      cand_idx[pos] = index_of(i);
+    } else {
+      kept[pos] = index_of(i);
+    }
+  };
+
+  if (n_top == 0) return;
+  if (n_top >= len) {  // everything is kept (direct or segment only: a merge always has more candidates)
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (i * kWave < lim) emit((uint32_t)(base + i * kWave + lane), i);
     return;
   }
-  if (a.n_top == 0) return;
-  const uint32_t n_top = (uint32_t)a.n_top;
 
   // 2. T = the n_top-th largest key
   uint32_t T = 0u, before;
@@ -224,10 +278,10 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
     uint32_t c = 0u;
 #pragma unroll
     for (int i = 0; i < E; ++i) c += key[i] >= cand ? 1u : 0u;
-    if (waves_sum(wave_count(c), s_red, before) >= n_top) T = cand;
+    if (waves_sum(wave_count(c), s_red, before) >= (uint32_t)n_top) T = cand;
   }
 
-  // 3. ascending emission
+  // 3. ascending emission: every key > T, and the k_rem lowest-index keys == T
   uint32_t gt_l = 0u, eq_l = 0u;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
@@ -236,7 +290,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   }
   const uint32_t gt = wave_count(gt_l), eq = wave_count(eq_l);
   uint32_t gt_before, eq_before;
-  const uint32_t k_rem = n_top - waves_sum(gt, s_red, gt_before);  // keys equal to T to take
+  const uint32_t k_rem = (uint32_t)n_top - waves_sum(gt, s_red, gt_before);
   waves_sum(eq, s_red, eq_before);
   const uint32_t eq_take = eq_before >= k_rem ? 0u : (k_rem - eq_before < eq ? k_rem - eq_before : eq);
   uint32_t run_sel;
@@ -249,26 +303,61 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
     const bool is_eq = key[i] == T;
     const bool take = key[i] > T || (is_eq && run_eq + (uint32_t)__popcll(m_eq & lower) < k_rem);
     const uint64_t m_take = __ballot(take);
-    if (take) kept[run_sel + (uint32_t)__popcll(m_take & lower)] = base + i * kWave + lane;
+    if (take) emit(run_sel + (uint32_t)__popcll(m_take & lower), i);
     run_eq += (uint32_t)__popcll(m_eq);
     run_sel += (uint32_t)__popcll(m_take);
   }
 }
 
+constexpr int kSelMaxPerLane = 64;
+
+static int per_lane(int64_t len) { return (int)((len + kSelThreads - 1) / kSelThreads); }
+
+int select_segments(int64_t n_units, int64_t n_pre, int64_t n_top) {
+  if (n_top <= 0 || n_top >= n_pre) return 1;
+  if (n_units >= 128 && per_lane(n_pre) <= kSelMaxPerLane) return 1;  // one block per unit fills the GPU
+  // Balance segment length against candidate count (B ~ sqrt(n / n_top)),
+  // within the register capacity of both stages.
+  int64_t b = (int64_t)(sqrt((double)n_pre / (double)n_top) + 0.5);
+  if (b < 2) b = 2;
+  while (b > 2 && b * n_top > (int64_t)kSelThreads * kSelMaxPerLane) --b;
+  while (per_lane((n_pre + b - 1) / b) > kSelMaxPerLane) ++b;
+  if (b * n_top > (int64_t)kSelThreads * kSelMaxPerLane) return 1;  // too many candidates: single stage
+  return (int)b;
+}
+
+size_t select_candidate_bytes(int64_t n_units, int64_t n_pre, int64_t n_top) {
+  const int b = select_segments(n_units, n_pre, n_top);
+  return b > 1 ? (size_t)(n_units * b * n_top) * 8 : 0;
+}
+
+template <int MODE, int R>
+static void launch_mode(const SelectArgs& a, dim3 grid, int len, hipStream_t s) {
+  const dim3 block(kSelThreads);
+  const int e = per_lane(len);
+  if (e <= 4) select_reg_kernel<4, R, MODE><<<grid, block, 0, s>>>(a);
+  else if (e <= 8) select_reg_kernel<8, R, MODE><<<grid, block, 0, s>>>(a);
+  else if (e <= 16) select_reg_kernel<16, R, MODE><<<grid, block, 0, s>>>(a);
+  else if (e <= 32) select_reg_kernel<32, R, MODE><<<grid, block, 0, s>>>(a);
+  else select_reg_kernel<64, R, MODE><<<grid, block, 0, s>>>(a);
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_units), block(kSelThreads);
-  const int64_t per_lane = ((int64_t)a.n_pre + kSelThreads - 1) / kSelThreads;
   const bool r3 = a.pool == 1 && a.pool_radius == 3;  // the width-7 max pool
-  if (per_lane <= 4) {
-    if (r3) select_reg_kernel<4, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<4, -1><<<grid, block, 0, s>>>(a);
-  } else if (per_lane <= 16) {
-    if (r3) select_reg_kernel<16, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<16, -1><<<grid, block, 0, s>>>(a);
-  } else if (per_lane <= 32) {
-    if (r3) select_reg_kernel<32, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<32, -1><<<grid, block, 0, s>>>(a);
-  } else if (per_lane <= 64) {
-    if (r3) select_reg_kernel<64, 3><<<grid, block, 0, s>>>(a); else select_reg_kernel<64, -1><<<grid, block, 0, s>>>(a);
+  if (a.n_seg > 1) {
+    const dim3 g1((unsigned)((int64_t)a.n_units * a.n_seg));
+    if (r3) launch_mode<kSelSegment, 3>(a, g1, a.seg_len, s);
+    else launch_mode<kSelSegment, -1>(a, g1, a.seg_len, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_mode<kSelMerge, -1>(a, dim3((unsigned)a.n_units), a.n_seg * a.n_top, s);
+    return hipGetLastError();
+  }
+  if (per_lane(a.n_pre) <= kSelMaxPerLane) {
+    if (r3) launch_mode<kSelDirect, 3>(a, dim3((unsigned)a.n_units), a.n_pre, s);
+    else launch_mode<kSelDirect, -1>(a, dim3((unsigned)a.n_units), a.n_pre, s);
   } else {
-    select_kernel<<<grid, block, 0, s>>>(a);
+    select_kernel<<<dim3((unsigned)a.n_units), dim3(kSelThreads), 0, s>>>(a);
   }
   return hipGetLastError();
 }
