@@ -327,14 +327,29 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreArgs a) {
   if (idx >= (int64_t)a.n_units * a.n_rows) return;
   const int64_t unit = idx / a.n_rows, r = idx % a.n_rows;
   const float2* p = a.part + unit * a.n_chunks * a.n_rows + r;
-  float M = -INFINITY;
-  for (int ch = 0; ch < a.n_chunks; ++ch) M = fmaxf(M, p[(int64_t)ch * a.n_rows].x);
-  float S = 0.f;
-  if (M != -INFINITY)
-    for (int ch = 0; ch < a.n_chunks; ++ch) {
-      const float2 v = p[(int64_t)ch * a.n_rows];
-      if (v.x != -INFINITY) S += v.y * exp2f(v.x - M);
+  // One pass over the chunk partials, eight loads in flight, merged in chunk
+  // order with a running maximum (fixed order: run-to-run identical).
+  constexpr int kBatch = 8;
+  float M = -INFINITY, S = 0.f;
+  for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kBatch) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      v[u] = p[(int64_t)min(ch0 + u, a.n_chunks - 1) * a.n_rows];  // clamped; extra ones dropped below
+      if (ch0 + u >= a.n_chunks) v[u] = make_float2(-INFINITY, 0.f);
     }
+    float mb = v[0].x;
+#pragma unroll
+    for (int u = 1; u < kBatch; ++u) mb = fmaxf(mb, v[u].x);
+    if (mb == -INFINITY) continue;
+    if (mb > M) {
+      S = (M == -INFINITY) ? 0.f : S * exp2f(M - mb);
+      M = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (v[u].x != -INFINITY) S += v[u].y * exp2f(v[u].x - M);
+  }
   a.lam[idx] = M + log2f(S);
 }
 
