@@ -43,7 +43,13 @@ namespace skv {
 #define SKV_WAVES 8
 #endif
 constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block per CU)
-constexpr int kMaxSubPerChunk = 16;          // groups of resident keys per block
+#ifndef SKV_MAX_SUB
+#define SKV_MAX_SUB 32
+#endif
+#ifndef SKV_TARGET_BLOCKS
+#define SKV_TARGET_BLOCKS 768
+#endif
+constexpr int kMaxSubPerChunk = SKV_MAX_SUB;  // groups of resident keys per block
 
 template <typename T, int D>
 struct ScoreGeom {
@@ -482,7 +488,7 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
   // Key chunks: enough blocks (units x chunks x parts) for several rounds over
   // the 256 CUs, one block per CU; at most kMaxSubPerChunk groups of resident
   // keys per block, so the parts of a chunk stay close together in time.
-  constexpr int64_t kTargetBlocks = 2048;
+  constexpr int64_t kTargetBlocks = SKV_TARGET_BLOCKS;
   const int64_t subs = (n_keys + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub;
   const int64_t ups = n_units * pl->n_parts;
   int64_t chunks = (kTargetBlocks + ups - 1) / ups;
