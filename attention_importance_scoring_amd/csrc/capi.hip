@@ -62,7 +62,7 @@ struct ScoreWs {
   size_t part, lam, colpart, end;
 };
 ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
-  ScorePlan pl{1, 1, 32, 1, 0, 0};
+  ScorePlan pl{1, 1, 32, 1, 2, 0, 0};
   if (keys > 0 && rows > 0) score_plan(d.dtype, (int)d.D, units, rows, keys, &pl);
   const int64_t chunks = pl.n_chunks;
   ScoreWs w;
@@ -161,7 +161,7 @@ void apply_plan(ScoreArgs& a, const ScorePlan& pl) {
 skv_status run_scoring(const Dims& d, ScoreArgs& a, const ScorePlan& pl, hipStream_t s) {
   {
     ProfScope p("score_pass1", s);
-    SKV_TRY(hip_status(launch_score_pass1(d.dtype, (int)d.D, a, pl.lds_pass1, s)));
+    SKV_TRY(hip_status(launch_score_pass1(d.dtype, (int)d.D, pl.kt, a, pl.lds_pass1, s)));
   }
   {
     ProfScope p("lse_combine", s);
@@ -262,7 +262,7 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   SKV_TRY(run_scoring(d, a, pl, s));
   {
     ProfScope p("score_pass2", s);
-    SKV_TRY(hip_status(launch_score_pass2(d.dtype, (int)d.D, a, pl.lds_pass2, s)));
+    SKV_TRY(hip_status(launch_score_pass2(d.dtype, (int)d.D, pl.kt, a, pl.lds_pass2, s)));
   }
   if (a.n_parts == 1) return SKV_OK;
   ProfScope p("colsum_combine", s);

@@ -38,12 +38,13 @@ struct ScoreArgs {
 // Work plan of the two scoring passes for one problem size.
 struct ScorePlan {
   int32_t n_sub, n_chunks, rows_per_part, n_parts;
+  int32_t kt;                   // key tiles of 32 per wave (2 or 4)
   size_t lds_pass1, lds_pass2;  // dynamic LDS bytes per block
 };
 void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl);
-hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
+hipError_t launch_score_pass1(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s);
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
-hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s);
+hipError_t launch_score_pass2(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s);
 hipError_t launch_colsum_combine(const ScoreArgs& a, hipStream_t s);  // when n_parts > 1
 
 // SpecPC pass 2: mean over (layer, query head) of the causal probabilities,

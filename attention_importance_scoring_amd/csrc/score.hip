@@ -31,13 +31,6 @@
 
 namespace skv {
 
-// Registers per lane that hold resident keys, and the most key tiles per wave.
-#ifndef SKV_KEY_VGPRS
-#define SKV_KEY_VGPRS 64
-#endif
-#ifndef SKV_MAX_KT
-#define SKV_MAX_KT 2
-#endif
 // Waves per block (one block per CU): 4 SIMDs x SKV_WAVES / 4 waves each.
 #ifndef SKV_WAVES
 #define SKV_WAVES 8
@@ -51,12 +44,12 @@ constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block
 #endif
 constexpr int kMaxSubPerChunk = SKV_MAX_SUB;  // groups of resident keys per block
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 struct ScoreGeom {
   using RF = RowFrag<T, D>;
   static constexpr int kNV = RF::kNV;
-  static constexpr int kKTraw = SKV_KEY_VGPRS / (4 * kNV);
-  static constexpr int kKT = kKTraw < 1 ? 1 : (kKTraw > SKV_MAX_KT ? SKV_MAX_KT : kKTraw);  // key tiles per wave
+  static constexpr int kKT = KT;  // key tiles (of 32) held per wave
+  static_assert(KT * 4 * kNV <= 128, "resident keys must fit in 128 VGPRs");
   static constexpr int kWaves = SKV_WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
@@ -88,9 +81,9 @@ __device__ __forceinline__ const char* unit_rows(const ScoreArgs& a, int unit) {
 
 // Copies rows [0, n_rows) starting at `src` into LDS (padded pitch) and zeroes
 // rows [n_rows, n_pad).  All threads of the block take part.
-template <typename T, int D>
+template <typename T, int D, int KT>
 __device__ __forceinline__ void stage_rows(char* s_q, const char* src, int n_rows, int n_pad) {
-  using Gm = ScoreGeom<T, D>;
+  using Gm = ScoreGeom<T, D, KT>;
   const int total = n_pad * Gm::kVecPerRow;
   for (int base = 0; base < total; base += 4 * Gm::kThreads) {
     u32x4 v[4];
@@ -112,9 +105,9 @@ __device__ __forceinline__ void stage_rows(char* s_q, const char* src, int n_row
 
 // This lane's MFMA operand vectors of row tile rt: vector v of the lane's
 // half row (row 32 rt + lane % 32).
-template <typename T, int D>
-__device__ __forceinline__ void read_q_frag(const char* s_q, int rt, int lane, u32x4 (&qf)[ScoreGeom<T, D>::kNV]) {
-  using Gm = ScoreGeom<T, D>;
+template <typename T, int D, int KT>
+__device__ __forceinline__ void read_q_frag(const char* s_q, int rt, int lane, u32x4 (&qf)[ScoreGeom<T, D, KT>::kNV]) {
+  using Gm = ScoreGeom<T, D, KT>;
   const char* p = s_q + (rt * 32 + lane % 32) * Gm::kRowPitch + (lane / 32) * Gm::RF::kHalfBytes;
 #pragma unroll
   for (int v = 0; v < Gm::kNV; ++v) qf[v] = *reinterpret_cast<const u32x4*>(p + v * 16);
@@ -123,10 +116,10 @@ __device__ __forceinline__ void read_q_frag(const char* s_q, int rt, int lane, u
 // Resident keys of this wave: kst[kt][v] = 16-byte vector v of the lane's
 // half row of key (kbase + 32 kt + lane % 32); zero beyond n_keys.  The loads
 // are unconditional (clamped address, then a select), so no branch is emitted.
-template <typename T, int D>
+template <typename T, int D, int KT>
 __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbase,
-                                          u32x4 (&kst)[ScoreGeom<T, D>::kKT][ScoreGeom<T, D>::kNV]) {
-  using Gm = ScoreGeom<T, D>;
+                                          u32x4 (&kst)[ScoreGeom<T, D, KT>::kKT][ScoreGeom<T, D, KT>::kNV]) {
+  using Gm = ScoreGeom<T, D, KT>;
   const int lane = threadIdx.x % kWave, half = lane / 32;
   const int layer = a.layer0 + unit / a.n_kv_heads;
   const int kvh = unit % a.n_kv_heads;
@@ -186,11 +179,11 @@ __device__ __forceinline__ BlockPos block_pos(const ScoreArgs& a) {
 // Pass 1
 
 // acc = K_tile x Q_tile^T for the wave's keys (M) and the tile's rows (N).
-template <typename T, int D, bool MASKED>
-__device__ __forceinline__ void pass1_mfma(const u32x4 (&kst)[ScoreGeom<T, D>::kKT][ScoreGeom<T, D>::kNV],
-                                           const u32x4 (&qf)[ScoreGeom<T, D>::kNV], int rel,
-                                           f32x16 (&acc)[ScoreGeom<T, D>::kKT]) {
-  using Gm = ScoreGeom<T, D>;
+template <typename T, int D, int KT, bool MASKED>
+__device__ __forceinline__ void pass1_mfma(const u32x4 (&kst)[ScoreGeom<T, D, KT>::kKT][ScoreGeom<T, D, KT>::kNV],
+                                           const u32x4 (&qf)[ScoreGeom<T, D, KT>::kNV], int rel,
+                                           f32x16 (&acc)[ScoreGeom<T, D, KT>::kKT]) {
+  using Gm = ScoreGeom<T, D, KT>;
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt) {
     if constexpr (MASKED) {
@@ -207,9 +200,9 @@ __device__ __forceinline__ void pass1_mfma(const u32x4 (&kst)[ScoreGeom<T, D>::k
 }
 
 // Per-lane (max, sum) of the lane's row over the wave's keys, both half-waves merged.
-template <typename T, int D, bool MASKED>
-__device__ __forceinline__ RowStat pass1_stats(const f32x16 (&acc)[ScoreGeom<T, D>::kKT], float c) {
-  using Gm = ScoreGeom<T, D>;
+template <typename T, int D, int KT, bool MASKED>
+__device__ __forceinline__ RowStat pass1_stats(const f32x16 (&acc)[ScoreGeom<T, D, KT>::kKT], float c) {
+  using Gm = ScoreGeom<T, D, KT>;
   float m4[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt)
@@ -232,9 +225,9 @@ __device__ __forceinline__ RowStat pass1_stats(const f32x16 (&acc)[ScoreGeom<T, 
 
 // Sum of 2^(c x - ref) over the wave's keys for the lane's row, both
 // half-waves added.  Masked entries (-inf) add 0 when ref is finite.
-template <typename T, int D>
-__device__ __forceinline__ float pass1_sum_ref(const f32x16 (&acc)[ScoreGeom<T, D>::kKT], float c, float ref) {
-  using Gm = ScoreGeom<T, D>;
+template <typename T, int D, int KT>
+__device__ __forceinline__ float pass1_sum_ref(const f32x16 (&acc)[ScoreGeom<T, D, KT>::kKT], float c, float ref) {
+  using Gm = ScoreGeom<T, D, KT>;
   float s4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s4[i] = fast_exp2(__builtin_fmaf(acc[0][i], c, -ref));
@@ -253,9 +246,9 @@ __device__ __forceinline__ RowStat renormalize(RowStat st) {
   return {st.m + (float)e, mant};
 }
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass1_kernel(ScoreArgs a) {
-  using Gm = ScoreGeom<T, D>;
+  using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                      // [rows_per_part][pitch]
   RowStat* s_ws = reinterpret_cast<RowStat*>(smem + (size_t)a.rows_per_part * Gm::kRowPitch);  // [waves][rows_per_part]
@@ -282,38 +275,38 @@ __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass1_kernel(ScoreArg
     const int n_tiles = (prow + 31) / 32;
     const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
     const int n_iter = n_sub * n_tiles;
-    stage_rows<T, D>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
+    stage_rows<T, D, KT>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     __syncthreads();
 
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
-    load_keys<T, D>(a, unit, wave_kbase(0), kst);
+    load_keys<T, D, KT>(a, unit, wave_kbase(0), kst);
     bool masked = false;
     for (int it = 0; it < n_iter; ++it) {
       const IterPos cu = iter_pos(it, n_tiles, rot);
       if (cu.j == 0) {  // new sub-chunk
-        if (cu.sc > 0) load_keys<T, D>(a, unit, wave_kbase(cu.sc), kst);
+        if (cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);
         masked = sub_masked(cu.sc);
       }
       u32x4 qf[Gm::kNV];
-      read_q_frag<T, D>(s_q, cu.rt, lane, qf);
+      read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
       f32x16 acc[Gm::kKT];
       const int r = cu.rt * 32 + lane % 32;
       if (masked)
-        pass1_mfma<T, D, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
+        pass1_mfma<T, D, KT, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
       else
-        pass1_mfma<T, D, false>(kst, qf, 0, acc);
+        pass1_mfma<T, D, KT, false>(kst, qf, 0, acc);
       RowStat st;
       if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
-        st = masked ? pass1_stats<T, D, true>(acc, c) : pass1_stats<T, D, false>(acc, c);
+        st = masked ? pass1_stats<T, D, KT, true>(acc, c) : pass1_stats<T, D, KT, false>(acc, c);
       } else {
         // Later visits sum against the row's running reference, which after
         // renormalization is within one of log2 of the sum so far: no per-tile
         // max and no rescaling.  A wave falls back to the exact merge when a
         // row has no reference yet or a tile would exceed it by 2^64.
         const RowStat cur = ws[r];  // lanes l and l ^ 32 read the same row
-        const float add = pass1_sum_ref<T, D>(acc, c, cur.m);
+        const float add = pass1_sum_ref<T, D, KT>(acc, c, cur.m);
         if (__any(!(add <= 0x1p64f)))
-          st = merge_stat(cur, pass1_stats<T, D, true>(acc, c));
+          st = merge_stat(cur, pass1_stats<T, D, KT, true>(acc, c));
         else
           st = {cur.m, cur.s + add};
       }
@@ -372,11 +365,11 @@ __global__ __launch_bounds__(256) void colsum_combine_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Pass 2
 
-template <typename T, int D>
-__device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D>::kKT][ScoreGeom<T, D>::kNV],
-                                           const u32x4 (&qf)[ScoreGeom<T, D>::kNV],
-                                           f32x16 (&acc)[ScoreGeom<T, D>::kKT]) {
-  using Gm = ScoreGeom<T, D>;
+template <typename T, int D, int KT>
+__device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D, KT>::kKT][ScoreGeom<T, D, KT>::kNV],
+                                           const u32x4 (&qf)[ScoreGeom<T, D, KT>::kNV],
+                                           f32x16 (&acc)[ScoreGeom<T, D, KT>::kKT]) {
+  using Gm = ScoreGeom<T, D, KT>;
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt) acc[kt] = f32x16{};
 #pragma unroll
@@ -385,9 +378,9 @@ __device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D>::k
     for (int kt = 0; kt < Gm::kKT; ++kt) acc[kt] = Mfma<T>::step(qf[v], kst[kt][v], acc[kt]);
 }
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArgs a) {
-  using Gm = ScoreGeom<T, D>;
+  using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                    // [rows_per_part][pitch]
   float* s_lam = reinterpret_cast<float*>(smem + (size_t)a.rows_per_part * Gm::kRowPitch);  // [rows_per_part]
@@ -423,17 +416,17 @@ __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArg
     const int n_tiles = (prow + 31) / 32;
     const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
     const int n_iter = n_sub * n_tiles;
-    stage_rows<T, D>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
+    stage_rows<T, D, KT>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     for (int r = threadIdx.x; r < n_tiles * 32; r += Gm::kThreads) s_lam[r] = (r < prow) ? lam_unit[row0 + r] : INFINITY;
     __syncthreads();
 
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
-    load_keys<T, D>(a, unit, wave_kbase(0), kst);
+    load_keys<T, D, KT>(a, unit, wave_kbase(0), kst);
     float colsum[Gm::kKT];
     for (int it = 0; it < n_iter; ++it) {
       const IterPos cu = iter_pos(it, n_tiles, rot);
       if (cu.j == 0) {  // new sub-chunk
-        if (cu.sc > 0) load_keys<T, D>(a, unit, wave_kbase(cu.sc), kst);
+        if (cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
       }
@@ -441,8 +434,8 @@ __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArg
       read_lam(cu.rt, lam);
       f32x16 acc[Gm::kKT];
       u32x4 qf[Gm::kNV];
-      read_q_frag<T, D>(s_q, cu.rt, lane, qf);
-      pass2_mfma<T, D>(kst, qf, acc);
+      read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
+      pass2_mfma<T, D, KT>(kst, qf, acc);
       // acc[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
 #pragma unroll
       for (int kt = 0; kt < Gm::kKT; ++kt) {
@@ -468,9 +461,9 @@ __global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArg
 
 // ---------------------------------------------------------------------------
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
-  using Gm = ScoreGeom<T, D>;
+  using Gm = ScoreGeom<T, D, KT>;
   // Row parts: as many 32-row tiles as the LDS budget holds, split evenly.
   const int64_t tiles = (n_rows + 31) / 32;
   const int64_t per_row1 = Gm::kRowPitch + (int64_t)Gm::kWaves * (int64_t)sizeof(RowStat);
@@ -497,15 +490,29 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
   if (per > kMaxSubPerChunk) per = kMaxSubPerChunk;
   pl->n_sub = (int32_t)per;
   pl->n_chunks = (int32_t)((subs + per - 1) / per);
+  pl->kt = KT;
+}
+
+// Four key tiles per wave halve the LDS reads of the row operand per MFMA,
+// but coarsen the key split: they are taken only where the resident-key
+// registers allow them and every block still walks many key groups.
+template <typename T, int D>
+static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
+  plan_for<T, D, 2>(n_units, n_rows, n_keys, pl);
+  if constexpr (4 * 4 * RowFrag<T, D>::kNV <= 128) {
+    ScorePlan p4;
+    plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4);
+    if (p4.n_sub >= 16) *pl = p4;
+  }
 }
 
 void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   if (dtype == 0) {
-    if (head_dim == 64) plan_for<float, 64>(n_units, n_rows, n_keys, pl);
-    else plan_for<float, 128>(n_units, n_rows, n_keys, pl);
+    if (head_dim == 64) plan_pick<float, 64>(n_units, n_rows, n_keys, pl);
+    else plan_pick<float, 128>(n_units, n_rows, n_keys, pl);
   } else {
-    if (head_dim == 64) plan_for<bf16_t, 64>(n_units, n_rows, n_keys, pl);
-    else plan_for<bf16_t, 128>(n_units, n_rows, n_keys, pl);
+    if (head_dim == 64) plan_pick<bf16_t, 64>(n_units, n_rows, n_keys, pl);
+    else plan_pick<bf16_t, 128>(n_units, n_rows, n_keys, pl);
   }
 }
 
@@ -515,27 +522,31 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 static hipError_t launch_p1(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  hipError_t e = allow_lds(score_pass1_kernel<T, D>, lds);
+  hipError_t e = allow_lds(score_pass1_kernel<T, D, KT>, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D>::kThreads);
-  score_pass1_kernel<T, D><<<grid, block, lds, s>>>(a);
+  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D, KT>::kThreads);
+  score_pass1_kernel<T, D, KT><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int KT>
 static hipError_t launch_p2(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  hipError_t e = allow_lds(score_pass2_kernel<T, D>, lds);
+  hipError_t e = allow_lds(score_pass2_kernel<T, D, KT>, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D>::kThreads);
-  score_pass2_kernel<T, D><<<grid, block, lds, s>>>(a);
+  const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D, KT>::kThreads);
+  score_pass2_kernel<T, D, KT><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_score_pass1(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s) {
-  if (dtype == 0) return head_dim == 64 ? launch_p1<float, 64>(a, lds, s) : launch_p1<float, 128>(a, lds, s);
-  return head_dim == 64 ? launch_p1<bf16_t, 64>(a, lds, s) : launch_p1<bf16_t, 128>(a, lds, s);
+hipError_t launch_score_pass1(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s) {
+  if (dtype == 0) {
+    if (head_dim == 64) return kt == 4 ? launch_p1<float, 64, 4>(a, lds, s) : launch_p1<float, 64, 2>(a, lds, s);
+    return launch_p1<float, 128, 2>(a, lds, s);
+  }
+  if (head_dim == 64) return kt == 4 ? launch_p1<bf16_t, 64, 4>(a, lds, s) : launch_p1<bf16_t, 64, 2>(a, lds, s);
+  return kt == 4 ? launch_p1<bf16_t, 128, 4>(a, lds, s) : launch_p1<bf16_t, 128, 2>(a, lds, s);
 }
 
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s) {
@@ -550,9 +561,13 @@ hipError_t launch_colsum_combine(const ScoreArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_pass2(int dtype, int head_dim, const ScoreArgs& a, size_t lds, hipStream_t s) {
-  if (dtype == 0) return head_dim == 64 ? launch_p2<float, 64>(a, lds, s) : launch_p2<float, 128>(a, lds, s);
-  return head_dim == 64 ? launch_p2<bf16_t, 64>(a, lds, s) : launch_p2<bf16_t, 128>(a, lds, s);
+hipError_t launch_score_pass2(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s) {
+  if (dtype == 0) {
+    if (head_dim == 64) return kt == 4 ? launch_p2<float, 64, 4>(a, lds, s) : launch_p2<float, 64, 2>(a, lds, s);
+    return launch_p2<float, 128, 2>(a, lds, s);
+  }
+  if (head_dim == 64) return kt == 4 ? launch_p2<bf16_t, 64, 4>(a, lds, s) : launch_p2<bf16_t, 64, 2>(a, lds, s);
+  return kt == 4 ? launch_p2<bf16_t, 128, 4>(a, lds, s) : launch_p2<bf16_t, 128, 2>(a, lds, s);
 }
 
 }  // namespace skv

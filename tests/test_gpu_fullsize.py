@@ -126,3 +126,26 @@ def test_specpc_draft_32k_full_stack_one_call():
     assert_scores_close(ts.cpu().numpy(), want, cfg.G, cfg.window, "token scores")
     pooled_o = oracle.pool1d(want, cfg.pool_kernel, "max")
     assert_kept_matches(kept.cpu().numpy()[None], pooled.cpu().numpy()[None], pooled_o[None], cfg.k_top, 0, "tokens")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_many_long_units_four_key_tiles_per_wave(dtype, d):
+    # 768 units of 16K keys: every block walks at least 16 groups of resident
+    # keys, which is where the planner holds four key tiles per wave.
+    cfg = wl.reduced(wl.CONFIGS[2], n_layers=96, n_q_heads=8, n_kv_heads=8, head_dim=d, dtype=dtype,
+                     n_in=16384 + 8, n_window=8, n_lookahead=4, C_max=200)
+    print(f"\n[case] {cfg.n_layers * cfg.n_kv_heads} units, {dtype} d={d}, n_in={cfg.n_in}", flush=True)
+    inp = wl.speckv_inputs(cfg, 31, "cuda")
+    L, H = cfg.n_layers, cfg.n_kv_heads
+    shape = shape_of(cfg, kv_head_stride=inp["kv_head_stride"])
+    ws = workspace(shape, cfg.C_max)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    scores = torch.full((L, H, cfg.n_pre), float("nan"), dtype=torch.float32, device="cuda")
+    pooled = torch.full_like(scores, float("nan"))
+    kept = torch.full((L, H, n_keep), -1, dtype=torch.int32, device="cuda")
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], scores, ws)
+    skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws)
+    torch.cuda.synchronize()
+    sc, pl, kp = scores.cpu().numpy(), pooled.cpu().numpy(), kept.cpu().numpy()
+    _check_every_unit(sc, pl, kp, cfg)
+    _check_sampled_units(sc, pl, kp, inp["q_obs"], inp["k"], cfg, [(0, 0), (47, 3), (95, 7)])
