@@ -31,10 +31,6 @@
 
 namespace skv {
 
-// Waves per block (one block per CU): 4 SIMDs x SKV_WAVES / 4 waves each.
-#ifndef SKV_WAVES
-#define SKV_WAVES 8
-#endif
 constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block per CU)
 #ifndef SKV_MAX_SUB
 #define SKV_MAX_SUB 32
@@ -50,7 +46,10 @@ struct ScoreGeom {
   static constexpr int kNV = RF::kNV;
   static constexpr int kKT = KT;  // key tiles (of 32) held per wave
   static_assert(KT * 4 * kNV <= 128, "resident keys must fit in 128 VGPRs");
-  static constexpr int kWaves = SKV_WAVES;
+  // Waves per block (one block per CU, kWaves / 4 per SIMD).  At head_dim 64
+  // the vector work outweighs the MFMAs, and with at most 64 VGPRs of
+  // resident keys three waves per SIMD fit and raise the issue rate.
+  static constexpr int kWaves = (D == 64 && KT * 4 * kNV <= 64) ? 12 : 8;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
   static constexpr int kKeysPerSub = kWaves * kKeysPerWave;  // keys resident in one block at a time
@@ -247,7 +246,7 @@ __device__ __forceinline__ RowStat renormalize(RowStat st) {
 }
 
 template <typename T, int D, int KT>
-__global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass1_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                      // [rows_per_part][pitch]
@@ -379,7 +378,7 @@ __device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D, KT
 }
 
 template <typename T, int D, int KT>
-__global__ __launch_bounds__(SKV_WAVES * 64, 1) void score_pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass2_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* s_q = smem;                                                                    // [rows_per_part][pitch]
