@@ -113,8 +113,10 @@ __device__ __forceinline__ void read_q_frag(const char* s_q, int rt, int lane, u
 }
 
 // Resident keys of this wave: kst[kt][v] = 16-byte vector v of the lane's
-// half row of key (kbase + 32 kt + lane % 32); zero beyond n_keys.  The loads
-// are unconditional (clamped address, then a select), so no branch is emitted.
+// half row of key (kbase + 32 kt + lane % 32).  Keys at or beyond n_keys read
+// the last key's row instead (clamped address, no branch): pass 1 masks them
+// through the accumulator's initial value and pass 2 never stores their
+// columns, so their contents do not matter.
 template <typename T, int D, int KT>
 __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbase,
                                           u32x4 (&kst)[ScoreGeom<T, D, KT>::kKT][ScoreGeom<T, D, KT>::kNV]) {
@@ -125,14 +127,10 @@ __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbas
   const char* kb = static_cast<const char*>(a.k) + (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt) {
-    const int key = kbase + kt * 32 + (lane % 32);
-    const bool ok = key < a.n_keys;
-    const char* row = kb + (int64_t)(ok ? key : a.n_keys - 1) * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
+    const int key = min(kbase + kt * 32 + (lane % 32), a.n_keys - 1);
+    const char* row = kb + (int64_t)key * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
 #pragma unroll
-    for (int v = 0; v < Gm::kNV; ++v) {
-      const u32x4 x = ldg16(row + v * 16);
-      kst[kt][v] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int v = 0; v < Gm::kNV; ++v) kst[kt][v] = ldg16(row + v * 16);
   }
 }
 
