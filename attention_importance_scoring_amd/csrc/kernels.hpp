@@ -55,6 +55,7 @@ struct SpecPCArgs {
   float* rowblock_max;      // [n_rowblocks][n_in] partial maxima (workspace)
   float* token_scores;      // [n_in]
   int32_t n_rowblocks;
+  int32_t maps_per_stage;   // set by the launcher
   float inv_maps;           // 1 / ((L - l_skip) * Hq)
 };
 int specpc_rows_per_block(int dtype, int head_dim);

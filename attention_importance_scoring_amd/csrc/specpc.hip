@@ -8,8 +8,9 @@
 //   acc[i][j] = sum over (layer, query head) of 2^(c <q_i, k_j> - lse_i)
 // in registers across all (layer, query head) pairs, with the keys of the
 // current (layer, KV head) resident as MFMA operands (shared by the G query
-// heads of the group) and the query rows streamed through LDS.  The
-// attention tensor itself is never stored.  At the end each lane owns one key
+// heads of the group) and the query rows streamed through LDS, a whole GQA
+// group per barrier where it fits.  The attention tensor itself is never
+// stored.  At the end each lane owns one key
 // column: it takes the weighted max over its rows; a tiny second kernel
 // takes the max over row blocks and applies the 1 / (layers x heads) mean.
 #include "common.hpp"
@@ -19,71 +20,98 @@
 
 namespace skv {
 
+#ifndef SKV_PC_RT
+#define SKV_PC_RT 1
+#endif
+#ifndef SKV_PC_WAVES
+#define SKV_PC_WAVES 8
+#endif
+
+constexpr int kPcLdsBudget = 150 * 1024;  // dynamic LDS per block (one block per CU)
+
 template <typename T, int D>
 struct PcGeom {
   using RF = RowFrag<T, D>;
   static constexpr int kNV = RF::kNV;
-  static constexpr int kKT = 2;          // key tiles per wave
-  static constexpr int kRT = 2;          // row tiles per block (64 window rows)
-  static constexpr int kWaves = 4;
+  static constexpr int kKT = kNV >= 8 ? 1 : 2;  // key tiles per wave (resident keys at most 32 VGPRs)
+  static constexpr int kRT = SKV_PC_RT;          // row tiles per block
+  static constexpr int kWaves = SKV_PC_WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
   static constexpr int kKeysPerBlock = kWaves * kKeysPerWave;
   static constexpr int kRowsPerBlock = 32 * kRT;
   static constexpr int kRowPitch = RF::kRowBytes + 16;
-  static constexpr int kTileBytes = kRowsPerBlock * kRowPitch;
+  static constexpr int kMapBytes = kRowsPerBlock * kRowPitch;       // one (layer, query head) map's rows
+  static constexpr int kMapLds = kMapBytes + kRowsPerBlock * 4;     // rows + their lse values
   static constexpr int kVecPerRow = RF::kRowBytes / 16;
-  static constexpr int kStageVecs = kRowsPerBlock * kVecPerRow / kThreads;
-  static_assert((kRowsPerBlock * kVecPerRow) % kThreads == 0, "tile must split evenly over the block");
+  static constexpr int kVecsPerMap = kRowsPerBlock * kVecPerRow;
+  static constexpr int kStageVecs = (kVecsPerMap + kThreads - 1) / kThreads;  // per thread per map
 };
 
+// Maps staged per barrier: a whole GQA group when it fits (double-buffered).
+template <typename T, int D>
+static int pc_maps_per_stage(int group) {
+  const int fit = kPcLdsBudget / (2 * PcGeom<T, D>::kMapLds);
+  return group < fit ? group : (fit < 1 ? 1 : fit);
+}
+
+// Block = (32 kRT window rows, 8 waves x 32 kKT keys).  The block walks the (layer, KV head)
+// units; per unit its waves hold their keys as MFMA operands and the G query
+// heads' rows stream through LDS, several maps per barrier, the next stage's
+// rows loading while the current one is computed.
 template <typename T, int D, bool MASKED>
-__global__ __launch_bounds__(256, 2) void specpc_pass2_kernel(SpecPCArgs pa, int kblock0, int n_kblocks_launch) {
+__global__ __launch_bounds__(SKV_PC_WAVES * 64, 1) void specpc_pass2_kernel(SpecPCArgs pa, int kblock0, int n_kblocks_launch) {
   using Gm = PcGeom<T, D>;
   const ScoreArgs& a = pa.sc;
-  __shared__ __attribute__((aligned(16))) char s_tile[2][Gm::kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_lam[2][Gm::kRowsPerBlock];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int mps = pa.maps_per_stage;
+  char* s_rows = smem;                                                          // [2][mps][kMapBytes]
+  float* s_lam = reinterpret_cast<float*>(smem + (size_t)2 * mps * Gm::kMapBytes);  // [2][mps][64]
 
   // This launch covers key blocks [kblock0, kblock0 + n_kblocks_launch) of every row block.
   const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int rb = logical / n_kblocks_launch, kblk = kblock0 + logical % n_kblocks_launch;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, half = lane / 32;
-  const int W = a.rows_per_qhead;
+  // The row blocks of one key block are neighbours (same XCD, same time): the keys come from L2 after the first.
+  const int rb = logical % pa.n_rowblocks, kblk = kblock0 + logical / pa.n_rowblocks;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, half = lane / 32;
+  const int W = a.rows_per_qhead, G = a.group;
   const int row0 = rb * Gm::kRowsPerBlock;                    // first window row of the block
   const int kbase = kblk * Gm::kKeysPerBlock + wave * Gm::kKeysPerWave;
-  const int n_iter = a.n_units * a.group;                     // (layer, KV head, group member)
+  const int spu = (G + mps - 1) / mps;                        // stages per (layer, KV head)
+  const int n_stages = a.n_units * spu;
   const float c = a.c;
 
   // Waves whose keys all lie after the last row's position see nothing (causal).
   const int64_t last_pos = a.pos_base + (int64_t)(row0 + Gm::kRowsPerBlock - 1);
   const bool wave_active = (int64_t)kbase <= last_pos && kbase < a.n_keys;
 
-  // Stage iteration `it`: query rows [row0, row0 + 64) of (layer, hq) and their lse.
-  auto load_stage = [&](int it, u32x4 (&st)[Gm::kStageVecs], float& lst) {
-    const int unit = it / a.group, g = it % a.group;
+  auto stage_maps = [&](int st) { return min(mps, G - (st % spu) * mps); };
+  // Rows (clamped to the window: rows past it get lse = +inf and add 0) and
+  // lse values of map m of stage st.
+  auto load_map = [&](int st, int m, u32x4 (&v)[Gm::kStageVecs], float& l) {
+    const int unit = st / spu, g = (st % spu) * mps + m;
     const int layer = a.layer0 + unit / a.n_kv_heads, kvh = unit % a.n_kv_heads;
     const char* qh = static_cast<const char*>(a.q) +
-                     (layer * a.q_layer_stride + (int64_t)(kvh * a.group + g) * a.q_head_stride) * Elem<T>::kBytes;
+                     (layer * a.q_layer_stride + (int64_t)(kvh * G + g) * a.q_head_stride) * Elem<T>::kBytes;
 #pragma unroll
     for (int p = 0; p < Gm::kStageVecs; ++p) {
-      const int idx = p * Gm::kThreads + threadIdx.x;
+      const int idx = min(p * Gm::kThreads + tid, Gm::kVecsPerMap - 1);
       const int row = idx / Gm::kVecPerRow, col = idx % Gm::kVecPerRow;
-      const int i = row0 + row;
-      st[p] = (i < W) ? ldg16(qh + (int64_t)i * Gm::RF::kRowBytes + col * 16) : u32x4{0u, 0u, 0u, 0u};
+      v[p] = ldg16(qh + (int64_t)min(row0 + row, W - 1) * Gm::RF::kRowBytes + col * 16);
     }
-    if (threadIdx.x < Gm::kRowsPerBlock) {
-      const int i = row0 + threadIdx.x;
-      lst = (i < W) ? a.lam[(int64_t)unit * a.n_rows + (int64_t)g * W + i] : INFINITY;
+    if (tid < Gm::kRowsPerBlock) {
+      const int i = row0 + tid;
+      l = (i < W) ? a.lam[(int64_t)unit * a.n_rows + (int64_t)g * W + i] : INFINITY;
     }
   };
-  auto store_stage = [&](int buf, const u32x4 (&st)[Gm::kStageVecs], float lst) {
+  auto store_map = [&](int buf, int m, const u32x4 (&v)[Gm::kStageVecs], float l) {
+    char* dst = s_rows + (size_t)(buf * mps + m) * Gm::kMapBytes;
 #pragma unroll
     for (int p = 0; p < Gm::kStageVecs; ++p) {
-      const int idx = p * Gm::kThreads + threadIdx.x;
+      const int idx = p * Gm::kThreads + tid;
       const int row = idx / Gm::kVecPerRow, col = idx % Gm::kVecPerRow;
-      *reinterpret_cast<u32x4*>(s_tile[buf] + row * Gm::kRowPitch + col * 16) = st[p];
+      if (idx < Gm::kVecsPerMap) *reinterpret_cast<u32x4*>(dst + row * Gm::kRowPitch + col * 16) = v[p];
     }
-    if (threadIdx.x < Gm::kRowsPerBlock) s_lam[buf][threadIdx.x] = lst;
+    if (tid < Gm::kRowsPerBlock) s_lam[(buf * mps + m) * Gm::kRowsPerBlock + tid] = l;
   };
 
   f32x16 acc[Gm::kRT][Gm::kKT];
@@ -91,76 +119,83 @@ __global__ __launch_bounds__(256, 2) void specpc_pass2_kernel(SpecPCArgs pa, int
   for (int r = 0; r < Gm::kRT; ++r)
 #pragma unroll
     for (int kt = 0; kt < Gm::kKT; ++kt) acc[r][kt] = f32x16{};
-
   u32x4 kst[Gm::kKT][Gm::kNV];
-  u32x4 st[Gm::kStageVecs];
-  float lst = INFINITY;
-  load_stage(0, st, lst);
-  store_stage(0, st, lst);
-  __syncthreads();
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const int unit = it / a.group;
-    if (it % a.group == 0 && wave_active) {
-      // New (layer, KV head): load this wave's resident keys.
-      const int layer = a.layer0 + unit / a.n_kv_heads, kvh = unit % a.n_kv_heads;
-      const char* kb = static_cast<const char*>(a.k) +
-                       (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
+  // acc[r][kt][i] += 2^(c <q_(row0 + 32 r + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)> - lse)
+  auto compute_map = [&](int buf, int m) {
+    const char* rows = s_rows + (size_t)(buf * mps + m) * Gm::kMapBytes;
+    const float* lams = s_lam + (buf * mps + m) * Gm::kRowsPerBlock;
 #pragma unroll
-      for (int kt = 0; kt < Gm::kKT; ++kt) {
-        const int key = kbase + kt * 32 + (lane % 32);
-        const char* row = kb + (int64_t)key * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
+    for (int r = 0; r < Gm::kRT; ++r) {
+      // Keys after a row's position start at -inf (causal mask), so they add 0.
+      f32x16 sacc[Gm::kKT];
+      if constexpr (!MASKED) {
 #pragma unroll
-        for (int v = 0; v < Gm::kNV; ++v)
-          kst[kt][v] = (key < a.n_keys) ? ldg16(row + v * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (it + 1 < n_iter) load_stage(it + 1, st, lst);
-
-    if (wave_active) {
-#pragma unroll
-      for (int r = 0; r < Gm::kRT; ++r) {
-        // Keys after a row's position start at -inf (causal mask), so they add 0.
-        f32x16 sacc[Gm::kKT];
-        if constexpr (!MASKED) {
-#pragma unroll
-          for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = f32x16{};
-        } else {
-          int64_t rel64 = a.pos_base + row0 + r * 32 + 4 * half - (kbase + (lane % 32));
-          rel64 = rel64 < -4096 ? -4096 : (rel64 > 4096 ? 4096 : rel64);
-          const int rel = (int)rel64;
-#pragma unroll
-          for (int kt = 0; kt < Gm::kKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              sacc[kt][i] = (kt * 32 - 8 * (i >> 2) - (i & 3) <= rel) ? 0.f : -INFINITY;
-        }
-        const char* trow = s_tile[buf] + (r * 32 + lane % 32) * Gm::kRowPitch + half * Gm::RF::kHalfBytes;
-#pragma unroll
-        for (int v = 0; v < Gm::kNV; ++v) {
-          const u32x4 qv = *reinterpret_cast<const u32x4*>(trow + v * 16);
-#pragma unroll
-          for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = Mfma<T>::step(qv, kst[kt][v], sacc[kt]);
-        }
-        // sacc[kt][i] = <q_(row0 + 32 r + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
-        float lam[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lam[buf][r * 32 + 8 * g4 + 4 * half]);
-          lam[4 * g4 + 0] = l4[0];
-          lam[4 * g4 + 1] = l4[1];
-          lam[4 * g4 + 2] = l4[2];
-          lam[4 * g4 + 3] = l4[3];
-        }
+        for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = f32x16{};
+      } else {
+        int64_t rel64 = a.pos_base + row0 + r * 32 + 4 * half - (kbase + (lane % 32));
+        rel64 = rel64 < -4096 ? -4096 : (rel64 > 4096 ? 4096 : rel64);
+        const int rel = (int)rel64;
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[r][kt][i] += fast_exp2(__builtin_fmaf(sacc[kt][i], c, -lam[i]));
-        __builtin_amdgcn_sched_barrier(0);  // keep the two row tiles' live ranges apart
+          for (int i = 0; i < 16; ++i) sacc[kt][i] = (kt * 32 - 8 * (i >> 2) - (i & 3) <= rel) ? 0.f : -INFINITY;
+      }
+      const char* trow = rows + (r * 32 + lane % 32) * Gm::kRowPitch + half * Gm::RF::kHalfBytes;
+#pragma unroll
+      for (int v = 0; v < Gm::kNV; ++v) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(trow + v * 16);
+#pragma unroll
+        for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = Mfma<T>::step(qv, kst[kt][v], sacc[kt]);
+      }
+      float lam[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lams[r * 32 + 8 * g4 + 4 * half]);
+        lam[4 * g4 + 0] = l4[0];
+        lam[4 * g4 + 1] = l4[1];
+        lam[4 * g4 + 2] = l4[2];
+        lam[4 * g4 + 3] = l4[3];
+      }
+#pragma unroll
+      for (int kt = 0; kt < Gm::kKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][kt][i] += fast_exp2(__builtin_fmaf(sacc[kt][i], c, -lam[i]));
+      __builtin_amdgcn_sched_barrier(0);  // keep the two row tiles' live ranges apart
+    }
+  };
+
+  u32x4 sv[Gm::kStageVecs];
+  float sl = INFINITY;
+  for (int m = 0; m < stage_maps(0); ++m) {
+    load_map(0, m, sv, sl);
+    store_map(0, m, sv, sl);
+  }
+  __syncthreads();
+
+  for (int st = 0; st < n_stages; ++st) {
+    const int buf = st & 1;
+    if (st % spu == 0 && wave_active) {
+      // New (layer, KV head): this wave's resident keys (clamped rows past n_keys are never stored).
+      const int unit = st / spu;
+      const int layer = a.layer0 + unit / a.n_kv_heads, kvh = unit % a.n_kv_heads;
+      const char* kb = static_cast<const char*>(a.k) + (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
+#pragma unroll
+      for (int kt = 0; kt < Gm::kKT; ++kt) {
+        const int key = min(kbase + kt * 32 + (lane % 32), a.n_keys - 1);
+        const char* row = kb + (int64_t)key * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
+#pragma unroll
+        for (int v = 0; v < Gm::kNV; ++v) kst[kt][v] = ldg16(row + v * 16);
       }
     }
-    if (it + 1 < n_iter) store_stage(buf ^ 1, st, lst);
+    const int n_cur = stage_maps(st);
+    const int n_nxt = st + 1 < n_stages ? stage_maps(st + 1) : 0;
+    const int n_m = n_cur > n_nxt ? n_cur : n_nxt;
+    for (int m = 0; m < n_m; ++m) {
+      if (m < n_nxt) load_map(st + 1, m, sv, sl);  // into the buffer nobody reads this stage
+      if (m < n_cur && wave_active) compute_map(buf, m);
+      if (m < n_nxt) store_map(buf ^ 1, m, sv, sl);
+    }
     __syncthreads();
   }
 
@@ -203,28 +238,39 @@ int specpc_keys_per_block(int dtype, int head_dim) {
 }
 
 template <typename T, int D>
-static void launch_pc2(const SpecPCArgs& a, hipStream_t s) {
+static hipError_t launch_pc2(const SpecPCArgs& args, hipStream_t s) {
   using Gm = PcGeom<T, D>;
+  SpecPCArgs a = args;
+  a.maps_per_stage = pc_maps_per_stage<T, D>(a.sc.group);
+  const size_t lds = (size_t)2 * a.maps_per_stage * Gm::kMapLds;
   const int n_kblocks = (a.sc.n_keys + Gm::kKeysPerBlock - 1) / Gm::kKeysPerBlock;
   // Key blocks whose every key precedes the first window position need no causal mask.
   int64_t n_plain = (a.sc.pos_base + 1) / Gm::kKeysPerBlock;
   if (n_plain > n_kblocks) n_plain = n_kblocks;
   if ((int64_t)n_kblocks * Gm::kKeysPerBlock > a.sc.n_keys && n_plain == n_kblocks) n_plain = n_kblocks - 1;
   const int n_masked = n_kblocks - (int)n_plain;
-  if (n_plain > 0)
-    specpc_pass2_kernel<T, D, false><<<dim3((unsigned)(n_plain * a.n_rowblocks)), dim3(Gm::kThreads), 0, s>>>(
+  if (n_plain > 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(specpc_pass2_kernel<T, D, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    specpc_pass2_kernel<T, D, false><<<dim3((unsigned)(n_plain * a.n_rowblocks)), dim3(Gm::kThreads), lds, s>>>(
         a, 0, (int)n_plain);
-  if (n_masked > 0)
-    specpc_pass2_kernel<T, D, true><<<dim3((unsigned)(n_masked * a.n_rowblocks)), dim3(Gm::kThreads), 0, s>>>(
+  }
+  if (n_masked > 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(specpc_pass2_kernel<T, D, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    specpc_pass2_kernel<T, D, true><<<dim3((unsigned)(n_masked * a.n_rowblocks)), dim3(Gm::kThreads), lds, s>>>(
         a, (int)n_plain, n_masked);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_specpc_pass2(int dtype, int head_dim, const SpecPCArgs& a, hipStream_t s) {
-  if (dtype == 0 && head_dim == 64) launch_pc2<float, 64>(a, s);
-  else if (dtype == 0) launch_pc2<float, 128>(a, s);
-  else if (head_dim == 64) launch_pc2<bf16_t, 64>(a, s);
-  else launch_pc2<bf16_t, 128>(a, s);
-  return hipGetLastError();
+  if (dtype == 0 && head_dim == 64) return launch_pc2<float, 64>(a, s);
+  if (dtype == 0) return launch_pc2<float, 128>(a, s);
+  if (head_dim == 64) return launch_pc2<bf16_t, 64>(a, s);
+  return launch_pc2<bf16_t, 128>(a, s);
 }
 
 hipError_t launch_specpc_reduce(const SpecPCArgs& a, hipStream_t s) {

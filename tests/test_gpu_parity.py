@@ -215,7 +215,8 @@ def _specpc_check(cfg, seed, weights=None):
     dict(n_layers=3, l_skip=1, n_in=1000, window=100, k_top=64),
     dict(n_layers=2, l_skip=0, n_in=777, window=1, k_top=700),
     dict(n_layers=2, l_skip=1, n_in=300, window=300, k_top=30),
-], ids=["ragged", "single-window-row", "window-equals-input"])
+    dict(n_layers=2, l_skip=0, n_in=900, window=77, k_top=64, head_dim=128),
+], ids=["ragged", "single-window-row", "window-equals-input", "d128-group-over-two-stages"])
 def test_specpc_small(case):
     _specpc_check(wl.reduced(wl.CONFIGS[5], **case), seed=21)
 
