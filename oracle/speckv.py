@@ -52,35 +52,51 @@ def row_probabilities(q_rows, k_prefix, scale: float) -> np.ndarray:
     return np.exp(s - lse)
 
 
-def head_scores(q_group, k_prefix, scale: float) -> np.ndarray:
+def head_scores(q_group, k_prefix, scale: float, aggregation: str = "sum") -> np.ndarray:
     """Importance of each remaining input key for one KV head.
 
     q_group: [G, n_obs, d], the observation queries of the G query heads that
     share this KV head (window rows then lookahead rows, the order does not
     matter); k_prefix: [n_pre, d].
 
-    score[j] = sum over query heads g and observation rows i of P_(g,i)[j].
+    aggregation "sum": score[j] = sum over query heads g and observation rows
+    i of P_(g,i)[j].
+    aggregation "max": score[j] = max over the same rows of P_(g,i)[j].
 
     Reading: the pages say the importance comes from the cross-attention of
-    the observation queries; the aggregation over queries and over the GQA
-    group is a plain sum (a mean would rank identically).
+    the observation queries; the default aggregation over queries and over
+    the GQA group is a plain sum (a mean would rank identically).  The "max"
+    variant takes the largest probability any observation row gives the key,
+    the reduction the pages' SpecPC paragraph applies across its query rows.
     """
+    if aggregation not in ("sum", "max"):
+        raise ValueError(aggregation)
     q = _as_f64(q_group)
     rows = q.reshape(-1, q.shape[-1])
     k = _as_f64(k_prefix)
     score = np.zeros(k.shape[0], dtype=np.float64)
     for r0 in range(0, rows.shape[0], _ROW_CHUNK):
-        score += row_probabilities(rows[r0:r0 + _ROW_CHUNK], k, scale).sum(axis=0)
+        p = row_probabilities(rows[r0:r0 + _ROW_CHUNK], k, scale)
+        if aggregation == "sum":
+            score += p.sum(axis=0)
+        else:
+            score = np.maximum(score, p.max(axis=0))
     return score
 
 
-def speckv_scores(q_obs, k, n_window: int, scale: float | None = None) -> np.ndarray:
-    """Scores for every layer and KV head.
+def speckv_scores(q_obs, k, n_window: int, scale: float | None = None, aggregation: str = "sum",
+                  per_query_head: bool = False) -> np.ndarray:
+    """Scores for every layer and KV head (or query head).
 
     q_obs: [L, Hq, n_obs, d]; k: [L, Hkv, n_in, d] (only the first
     n_pre = n_in - n_window rows of each head are scored).
     Query head hq belongs to KV head hq // G with G = Hq / Hkv.
-    Returns float64 [L, Hkv, n_pre].
+    Returns float64 [L, Hkv, n_pre], or [L, Hq, n_pre] with per_query_head,
+    where query head hq is scored alone against its KV head's keys.
+
+    Reading (per_query_head): the pages estimate importance "for each
+    attention head"; the default keeps one set per KV head, shared by its
+    query heads, and this variant keeps one per query head.
     """
     L, Hq, _, d = q_obs.shape
     Lk, Hkv, n_in, dk = k.shape
@@ -88,10 +104,16 @@ def speckv_scores(q_obs, k, n_window: int, scale: float | None = None) -> np.nda
     G = Hq // Hkv
     n_pre = n_in - n_window
     tau = default_scale(d) if scale is None else float(scale)
+    if per_query_head:
+        out = np.empty((L, Hq, n_pre), dtype=np.float64)
+        for layer in range(L):
+            for hq in range(Hq):
+                out[layer, hq] = head_scores(q_obs[layer, hq:hq + 1], k[layer, hq // G, :n_pre], tau, aggregation)
+        return out
     out = np.empty((L, Hkv, n_pre), dtype=np.float64)
     for layer in range(L):
         for h in range(Hkv):
-            out[layer, h] = head_scores(q_obs[layer, h * G:(h + 1) * G], k[layer, h, :n_pre], tau)
+            out[layer, h] = head_scores(q_obs[layer, h * G:(h + 1) * G], k[layer, h, :n_pre], tau, aggregation)
     return out
 
 
@@ -179,13 +201,18 @@ def compact_rows(rows, kept) -> np.ndarray:
 
 
 def speckv_compact(k, v, kept):
-    """k, v: [L, Hkv, n_in, d]; kept: [L, Hkv, n_keep].
-    Returns (k_c, v_c) of shape [L, Hkv, n_keep, d], same dtype as the input."""
-    L, Hkv = kept.shape[:2]
-    kc = np.empty((L, Hkv, kept.shape[2]) + k.shape[3:], dtype=k.dtype)
-    vc = np.empty((L, Hkv, kept.shape[2]) + v.shape[3:], dtype=v.dtype)
+    """k, v: [L, Hkv, n_in, d]; kept: [L, H, n_keep] with H = Hkv (one kept
+    set per KV head) or H = Hq, a multiple of Hkv (one per query head, taken
+    from KV head hq // (Hq / Hkv)).
+    Returns (k_c, v_c) of shape [L, H, n_keep, d], same dtype as the input."""
+    L, H = kept.shape[:2]
+    Hkv = k.shape[1]
+    assert H % Hkv == 0
+    rep = H // Hkv
+    kc = np.empty((L, H, kept.shape[2]) + k.shape[3:], dtype=k.dtype)
+    vc = np.empty((L, H, kept.shape[2]) + v.shape[3:], dtype=v.dtype)
     for layer in range(L):
-        for h in range(Hkv):
-            kc[layer, h] = compact_rows(k[layer, h], kept[layer, h])
-            vc[layer, h] = compact_rows(v[layer, h], kept[layer, h])
+        for h in range(H):
+            kc[layer, h] = compact_rows(k[layer, h // rep], kept[layer, h])
+            vc[layer, h] = compact_rows(v[layer, h // rep], kept[layer, h])
     return kc, vc

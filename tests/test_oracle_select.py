@@ -120,6 +120,23 @@ def test_compact_rows_encode_their_index():
     np.testing.assert_array_equal(kc[..., 2], np.broadcast_to(np.arange(L)[:, None, None], kept.shape))
 
 
+def test_compact_per_query_head_reads_its_kv_head():
+    # kept sets per query head: 6 query heads over 2 KV heads, head hq reads KV head hq // 3
+    L, Hkv, G, n_in, d = 2, 2, 3, 30, 4
+    k = np.zeros((L, Hkv, n_in, d), dtype=np.float32)
+    k[..., 0] = np.arange(n_in)
+    k[..., 1] = np.arange(Hkv)[None, :, None]
+    v = k + 0.5
+    rng = np.random.default_rng(1)
+    kept = np.stack([np.stack([np.sort(rng.choice(n_in, 5, replace=False)) for _ in range(Hkv * G)])
+                     for _ in range(L)])
+    kc, vc = oracle.speckv_compact(k, v, kept)
+    assert kc.shape == (L, Hkv * G, 5, d)
+    np.testing.assert_array_equal(kc[..., 0], kept)
+    np.testing.assert_array_equal(kc[..., 1], np.broadcast_to((np.arange(Hkv * G) // G)[None, :, None], kept.shape))
+    np.testing.assert_array_equal(vc - kc, 0.5)
+
+
 def test_kv_cache_size_closed_form_from_the_pages():
     with open(os.path.join(GOLDEN, "kv_cache_size_llama8b_128k.json")) as f:
         g = json.load(f)

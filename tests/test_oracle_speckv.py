@@ -180,3 +180,70 @@ def test_planted_heavy_hitters_recovered_tiny_config():
     planted = np.nonzero(norms > 2.5 * math.sqrt(cfg.head_dim))[0]
     assert len(planted) == 9 and planted[0] == 0
     assert set(planted.tolist()) <= set(kept[0, 0].tolist())
+
+
+# ---- variants: max over the observation rows, one kept set per query head ----
+
+def test_max_aggregation_hand_example():
+    # Same rows as the hand example: softmax rows (3/5, 1/5, 1/5) and (1/4, 1/2, 1/4),
+    # so the column maxima are (3/5, 1/2, 1/4).
+    d = 4
+    k = np.zeros((1, 1, 4, d))
+    k[0, 0, 0, 0] = 2 * math.log(3)
+    k[0, 0, 1, 1] = 2 * math.log(2)
+    k[0, 0, 3] = [100.0, 100.0, 0.0, 0.0]
+    q = np.zeros((1, 1, 2, d))
+    q[0, 0, 0, 0] = 1.0
+    q[0, 0, 1, 1] = 1.0
+    got = oracle.speckv_scores(q, k, n_window=1, aggregation="max")
+    np.testing.assert_allclose(got[0, 0], [0.6, 0.5, 0.25], rtol=0, atol=1e-15)
+
+
+def test_max_aggregation_equal_keys_is_uniform_probability():
+    # every row is uniform over the n_pre keys, so every column maximum is 1 / n_pre
+    q = _rand((1, 3, 4, 8), 5)
+    k = np.tile(_rand((1, 1, 1, 8), 6), (1, 1, 50, 1))
+    got = oracle.speckv_scores(q, k, n_window=10, aggregation="max")
+    np.testing.assert_allclose(got, 1.0 / 40, rtol=1e-13)
+
+
+def test_max_aggregation_single_row_equals_sum():
+    q = _rand((2, 1, 1, 16), 7)
+    k = _rand((2, 1, 30, 16), 8)
+    np.testing.assert_allclose(oracle.speckv_scores(q, k, 4, aggregation="max"), oracle.speckv_scores(q, k, 4),
+                               rtol=1e-14)
+
+
+def test_per_query_head_scores_add_up_to_kv_head_scores():
+    # the KV-head sum runs over the group's query heads, so it is the sum of the per-head scores
+    q = _rand((2, 6, 5, 16), 9)
+    k = _rand((2, 2, 40, 16), 10) * 2
+    per_head = oracle.speckv_scores(q, k, 7, per_query_head=True)
+    grouped = oracle.speckv_scores(q, k, 7)
+    assert per_head.shape == (2, 6, 33)
+    np.testing.assert_allclose(per_head.reshape(2, 2, 3, 33).sum(axis=2), grouped, rtol=1e-13)
+    np.testing.assert_allclose(per_head.sum(-1), 5.0, rtol=1e-13)  # n_obs rows per query head
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bruteforce_max_and_per_query_head_tiny(seed):
+    rng = np.random.default_rng(seed)
+    L, Hkv, G, n_obs, d, n_in, n_window = 2, 2, 3, 3, 4, 10, 2
+    q = rng.standard_normal((L, Hkv * G, n_obs, d)) * 2
+    k = rng.standard_normal((L, Hkv, n_in, d)) * 2
+    n_pre = n_in - n_window
+    want_max = np.zeros((L, Hkv, n_pre))
+    want_pqh = np.zeros((L, Hkv * G, n_pre))
+    for l in range(L):
+        for hq in range(Hkv * G):
+            h = hq // G
+            for i in range(n_obs):
+                logits = [0.5 * math.fsum(q[l, hq, i, t] * k[l, h, j, t] for t in range(d)) for j in range(n_pre)]
+                m = max(logits)
+                z = math.fsum(math.exp(x - m) for x in logits)
+                for j in range(n_pre):
+                    p = math.exp(logits[j] - m) / z
+                    want_max[l, h, j] = max(want_max[l, h, j], p)
+                    want_pqh[l, hq, j] += p
+    np.testing.assert_allclose(oracle.speckv_scores(q, k, n_window, aggregation="max"), want_max, rtol=1e-12)
+    np.testing.assert_allclose(oracle.speckv_scores(q, k, n_window, per_query_head=True), want_pqh, rtol=1e-12)
