@@ -11,12 +11,12 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import SKV_BF16, SKV_F32, SKV_POOL_AVG, SKV_POOL_MAX, SKV_POOL_NONE, Shape  # noqa: F401
+from ._lib import SKV_AGG_MAX, SKV_AGG_SUM, SKV_BF16, SKV_F32, SKV_POOL_AVG, SKV_POOL_MAX, SKV_POOL_NONE, Shape  # noqa: F401
 
 __all__ = [
     "Shape", "SpecKVError", "make_shape", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores",
     "speckv_select", "speckv_compact", "specpc_token_scores", "profile_enable", "profile_read",
-    "SKV_F32", "SKV_BF16", "SKV_POOL_NONE", "SKV_POOL_MAX", "SKV_POOL_AVG",
+    "SKV_F32", "SKV_BF16", "SKV_POOL_NONE", "SKV_POOL_MAX", "SKV_POOL_AVG", "SKV_AGG_SUM", "SKV_AGG_MAX",
 ]
 
 
@@ -33,8 +33,9 @@ def _check(status: int, where: str):
 
 
 def make_shape(n_layers, n_q_heads, n_kv_heads, head_dim, n_in, n_window, n_lookahead, dtype,
-               kv_head_stride=0, scale=0.0) -> Shape:
-    return Shape(n_layers, n_q_heads, n_kv_heads, head_dim, n_in, kv_head_stride, n_window, n_lookahead, scale, dtype)
+               kv_head_stride=0, scale=0.0, aggregation=0, per_query_head=0) -> Shape:
+    return Shape(n_layers, n_q_heads, n_kv_heads, head_dim, n_in, kv_head_stride, n_window, n_lookahead, scale, dtype,
+                 aggregation, per_query_head)
 
 
 def _ptr(t, name):

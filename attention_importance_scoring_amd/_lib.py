@@ -18,6 +18,7 @@ STATUS_NAMES = {
 }
 SKV_F32, SKV_BF16 = 0, 1
 SKV_POOL_NONE, SKV_POOL_MAX, SKV_POOL_AVG = 0, 1, 2
+SKV_AGG_SUM, SKV_AGG_MAX = 0, 1
 
 # Every symbol include/speckv.h declares.
 EXPORTED = (
@@ -31,7 +32,7 @@ class Shape(ctypes.Structure):
     _fields_ = [
         ("n_layers", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
         ("n_in", c_int64), ("kv_head_stride", c_int64), ("n_window", c_int32), ("n_lookahead", c_int32),
-        ("scale", c_float), ("dtype", c_int32),
+        ("scale", c_float), ("dtype", c_int32), ("aggregation", c_int32), ("per_query_head", c_int32),
     ]
 
 

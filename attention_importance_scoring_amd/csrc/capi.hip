@@ -27,6 +27,11 @@ struct Dims {
   int64_t L, Hq, Hkv, D, n_in, stride, n_window, n_lookahead, esize;
   float scale;
   int dtype;
+  int agg;   // skv_agg
+  bool pqh;  // per_query_head: SpecKV heads are the query heads
+  int64_t heads() const { return pqh ? Hq : Hkv; }     // SpecKV heads H per layer
+  int64_t group() const { return pqh ? 1 : Hq / Hkv; }  // query heads per SpecKV head
+  int64_t repeat() const { return pqh ? Hq / Hkv : 1; } // SpecKV heads per KV head
 };
 
 skv_status check_shape(const skv_shape* s, Dims* d) {
@@ -38,6 +43,10 @@ skv_status check_shape(const skv_shape* s, Dims* d) {
   if (s->n_in < 1 || s->n_in > INT32_MAX - 1024) return SKV_ERR_SHAPE;
   if (s->n_window < 0 || s->n_lookahead < 0 || s->n_window > s->n_in) return SKV_ERR_SHAPE;
   if (!(s->scale >= 0.f) || std::isinf(s->scale)) return SKV_ERR_PARAM;
+  if (s->aggregation != SKV_AGG_SUM && s->aggregation != SKV_AGG_MAX) return SKV_ERR_PARAM;
+  if (s->per_query_head != 0 && s->per_query_head != 1) return SKV_ERR_PARAM;
+  d->agg = s->aggregation;
+  d->pqh = s->per_query_head != 0;
   d->L = s->n_layers;
   d->Hq = s->n_q_heads;
   d->Hkv = s->n_kv_heads;
@@ -53,7 +62,7 @@ skv_status check_shape(const skv_shape* s, Dims* d) {
   d->dtype = s->dtype;
   const int64_t G = d->Hq / d->Hkv;
   // row counts and unit counts must stay inside int32 for the kernels
-  if (G * (d->n_window + d->n_lookahead) > INT32_MAX / 2 || d->L * d->Hkv > INT32_MAX / 2) return SKV_ERR_SHAPE;
+  if (G * (d->n_window + d->n_lookahead) > INT32_MAX / 2 || d->L * d->Hq > INT32_MAX / 2) return SKV_ERR_SHAPE;
   return SKV_OK;
 }
 
@@ -208,13 +217,13 @@ skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t*
   SKV_TRY(check_shape(shape, &d));
   if (!out) return SKV_ERR_NULL;
   if (C_max < 0) return SKV_ERR_PARAM;
-  const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
+  const int64_t units = d.L * d.heads(), G = d.group();
   const int64_t n_pre = d.n_in - d.n_window;
   size_t need = score_ws(d, units, G * (d.n_window + d.n_lookahead), n_pre).end;           // speckv_scores
   need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)) +                   // speckv_select
                             select_candidate_bytes(units, n_pre, keep_count(d, C_max) - d.n_window));
   need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
-  if (d.n_window >= 1) need = std::max(need, specpc_ws(d, units).end);                         // specpc_token_scores
+  if (d.n_window >= 1) need = std::max(need, specpc_ws(d, d.L * d.Hkv).end);                   // specpc_token_scores
   *out = need;
   return SKV_OK;
 }
@@ -226,9 +235,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   if (!q_obs || !k || !scores) return SKV_ERR_NULL;
   const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
   if (n_obs < 1) return SKV_ERR_SHAPE;
-  if ((d.Hq / d.Hkv) * n_obs > kMaxRows) return SKV_ERR_SHAPE;
+  if (d.group() * n_obs > kMaxRows) return SKV_ERR_SHAPE;
   if (!aligned(q_obs, 16) || !aligned(k, 16) || !aligned(scores, 4)) return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.Hkv, G = d.Hq / d.Hkv;
+  const int64_t units = d.L * d.heads(), G = d.group();
   const ScoreWs w = score_ws(d, units, G * n_obs, n_pre);
   if (n_pre == 0) return SKV_OK;
   if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
@@ -243,7 +252,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.k_layer_stride = d.Hkv * d.stride;
   a.layer0 = 0;
   a.n_units = (int32_t)units;
-  a.n_kv_heads = (int32_t)d.Hkv;
+  a.n_kv_heads = (int32_t)d.heads();
+  a.kv_repeat = (int32_t)d.repeat();
+  a.agg_max = d.agg == SKV_AGG_MAX;
   a.group = (int32_t)G;
   a.rows_per_qhead = (int32_t)n_obs;
   a.n_rows = (int32_t)(G * n_obs);
@@ -278,7 +289,7 @@ skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_
   if (pool != SKV_POOL_NONE && pool != SKV_POOL_MAX && pool != SKV_POOL_AVG) return SKV_ERR_PARAM;
   if (pool != SKV_POOL_NONE && (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 4097)) return SKV_ERR_PARAM;
   if (!aligned(scores, 4) || !aligned(kept, 4) || (pooled && !aligned(pooled, 4))) return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.Hkv, n_pre = d.n_in - d.n_window;
+  const int64_t units = d.L * d.heads(), n_pre = d.n_in - d.n_window;
   const int64_t n_keep = keep_count(d, C_max);
   if (pooled && ranges_overlap(pooled, (size_t)(units * n_pre) * 4, scores, (size_t)(units * n_pre) * 4))
     return SKV_ERR_ALIAS;
@@ -324,15 +335,19 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
   if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4))
     return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.Hkv, row_bytes = d.D * d.esize;
-  const size_t in_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * row_bytes);
+  const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
+  const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + d.n_in * row_bytes);
   const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
   const bool k_inplace = (k_out == k), v_inplace = (v_out == v);
   if (k_inplace != v_inplace) return SKV_ERR_ALIAS;
   if (k == v) return SKV_ERR_ALIAS;
+  if (k_inplace && units != kv_units) return SKV_ERR_PARAM;  // per-query-head caches do not fit the KV slabs
   hipStream_t s = static_cast<hipStream_t>(stream);
   GatherArgs g{};
   g.n_units = (int32_t)units;
+  g.units_per_layer = (int32_t)d.heads();
+  g.src_units_per_layer = (int32_t)d.Hkv;
+  g.src_repeat = (int32_t)d.repeat();
   g.n_rows = (int32_t)n_keep;
   g.n_src_rows = (int32_t)d.n_in;
   g.row_bytes = (int32_t)row_bytes;
@@ -378,6 +393,8 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
   ProfScope p("compact_copyback", s);
   GatherArgs b{};
   b.n_units = (int32_t)units;
+  b.units_per_layer = b.src_units_per_layer = (int32_t)d.Hkv;
+  b.src_repeat = 1;
   b.n_rows = (int32_t)n_keep;
   b.n_src_rows = (int32_t)n_keep;
   b.row_bytes = (int32_t)row_bytes;
@@ -399,6 +416,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   SKV_TRY(check_shape(shape, &d));
   if (!q_win || !k || !token_scores) return SKV_ERR_NULL;
   if (l_skip < 0 || l_skip >= d.L) return SKV_ERR_PARAM;
+  if (d.agg != SKV_AGG_SUM || d.pqh) return SKV_ERR_PARAM;  // SpecPC has its own aggregation
   const int64_t W = d.n_window;
   if (W < 1) return SKV_ERR_SHAPE;
   if ((d.Hq / d.Hkv) * W > kMaxRows) return SKV_ERR_SHAPE;
@@ -421,6 +439,8 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   a.layer0 = l_skip;
   a.n_units = (int32_t)units;
   a.n_kv_heads = (int32_t)d.Hkv;
+  a.kv_repeat = 1;
+  a.agg_max = 0;
   a.group = (int32_t)G;
   a.rows_per_qhead = (int32_t)W;
   a.n_rows = (int32_t)(G * W);

@@ -16,8 +16,10 @@ struct ScoreArgs {
   int64_t k_layer_stride;   // elements
   int64_t k_head_stride;    // elements
   int32_t layer0;           // first layer scored (SpecPC: l_skip)
-  int32_t n_units;          // (layers - layer0) * Hkv
-  int32_t n_kv_heads;
+  int32_t n_units;          // (layers - layer0) * heads per layer
+  int32_t n_kv_heads;       // heads per layer (unit % n_kv_heads is the head)
+  int32_t kv_repeat;        // heads per KV head (>1: one unit per query head); KV head = head / kv_repeat
+  int32_t agg_max;          // pass 2 aggregates the rows by max instead of sum
   int32_t group;            // G = Hq / Hkv
   int32_t rows_per_qhead;   // SpecKV: n_window + n_lookahead; SpecPC: W
   int32_t n_rows;           // R = G * rows_per_qhead
@@ -32,7 +34,7 @@ struct ScoreArgs {
   float2* part;             // pass 1 output: [n_units][n_chunks][R] (max, sum) in log2 units
   float* lam;               // combine output / pass 2 input: [n_units][R] log2-domain lse
   float* scores;            // pass 2 output: [n_units][n_keys]
-  float* colpart;           // pass 2, parts 1 ..: [n_parts - 1][n_units][n_keys] column sums
+  float* colpart;           // pass 2, parts 1 ..: [n_parts - 1][n_units][n_keys] column sums (or maxima)
 };
 
 // Work plan of the two scoring passes for one problem size.
@@ -94,7 +96,10 @@ struct GatherArgs {
   const int32_t* idx;       // [n_units][n_rows] or nullptr
   int64_t src_unit_stride;  // bytes
   int64_t dst_unit_stride;  // bytes
-  int32_t n_units;
+  int32_t n_units;          // destination units
+  int32_t units_per_layer;  // destination units per layer
+  int32_t src_units_per_layer;
+  int32_t src_repeat;       // destination units per source unit within a layer
   int32_t n_rows;           // rows per unit to write
   int32_t n_src_rows;       // valid source rows per unit (bounds check)
   int32_t row_bytes;        // multiple of 16

@@ -68,14 +68,15 @@ __device__ __forceinline__ RowStat merge_stat(RowStat a, RowStat b) {
   return {M, a.s * fast_exp2(a.m - M) + b.s * fast_exp2(b.m - M)};
 }
 
-// The query rows of one unit are contiguous: [G][rows_per_qhead][D], so row
-// r of the unit sits at r * D elements from the unit's first row.
+// The query rows of one unit are contiguous: [group][rows_per_qhead][D] (the
+// unit's query heads), so row r of the unit sits at r * D elements from the
+// unit's first row.
 template <typename T>
 __device__ __forceinline__ const char* unit_rows(const ScoreArgs& a, int unit) {
   const int layer = a.layer0 + unit / a.n_kv_heads;
-  const int kvh = unit % a.n_kv_heads;
+  const int head = unit % a.n_kv_heads;
   return static_cast<const char*>(a.q) +
-         (layer * a.q_layer_stride + (int64_t)kvh * a.group * a.q_head_stride) * Elem<T>::kBytes;
+         (layer * a.q_layer_stride + (int64_t)head * a.group * a.q_head_stride) * Elem<T>::kBytes;
 }
 
 // Copies rows [0, n_rows) starting at `src` into LDS (padded pitch) and zeroes
@@ -123,7 +124,7 @@ __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbas
   using Gm = ScoreGeom<T, D, KT>;
   const int lane = threadIdx.x % kWave, half = lane / 32;
   const int layer = a.layer0 + unit / a.n_kv_heads;
-  const int kvh = unit % a.n_kv_heads;
+  const int kvh = (unit % a.n_kv_heads) / a.kv_repeat;
   const char* kb = static_cast<const char*>(a.k) + (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt) {
@@ -349,13 +350,17 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreArgs a) {
   a.lam[idx] = M + log2f(S);
 }
 
-// scores += column sums of parts 1 .. n_parts - 1, in part order.
+// scores += column sums of parts 1 .. n_parts - 1, in part order (or their
+// maximum, for the max aggregation).
 __global__ __launch_bounds__(256) void colsum_combine_kernel(ScoreArgs a) {
   const int64_t n = (int64_t)a.n_units * a.n_keys;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   float v = a.scores[idx];
-  for (int p = 1; p < a.n_parts; ++p) v += a.colpart[(int64_t)(p - 1) * n + idx];
+  for (int p = 1; p < a.n_parts; ++p) {
+    const float x = a.colpart[(int64_t)(p - 1) * n + idx];
+    v = a.agg_max ? fmaxf(v, x) : v + x;
+  }
   a.scores[idx] = v;
 }
 
@@ -375,7 +380,14 @@ __device__ __forceinline__ void pass2_mfma(const u32x4 (&kst)[ScoreGeom<T, D, KT
     for (int kt = 0; kt < Gm::kKT; ++kt) acc[kt] = Mfma<T>::step(qf[v], kst[kt][v], acc[kt]);
 }
 
-template <typename T, int D, int KT>
+// Row aggregation of pass 2: sum (the default) or max of the probabilities.
+template <bool MAX>
+__device__ __forceinline__ float agg2(float x, float y) {
+  if constexpr (MAX) return fmaxf(x, y);
+  return x + y;
+}
+
+template <typename T, int D, int KT, bool MAX>
 __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass2_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -440,14 +452,14 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
 #pragma unroll
         for (int i = 0; i < 4; ++i) s4[i] = fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i]));
 #pragma unroll
-        for (int i = 4; i < 16; ++i) s4[i & 3] += fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i]));
-        colsum[kt] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        for (int i = 4; i < 16; ++i) s4[i & 3] = agg2<MAX>(s4[i & 3], fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i])));
+        colsum[kt] = agg2<MAX>(colsum[kt], agg2<MAX>(agg2<MAX>(s4[0], s4[1]), agg2<MAX>(s4[2], s4[3])));
       }
       if (cu.j + 1 == n_tiles) {  // sub-chunk complete for this part
         const int kbase = wave_kbase(cu.sc);
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt) {
-          const float tot = colsum[kt] + shfl_xor32(colsum[kt]);
+          const float tot = agg2<MAX>(colsum[kt], shfl_xor32(colsum[kt]));
           const int key = kbase + kt * 32 + lane;
           if (lane < 32 && key < a.n_keys) out[key] = tot;
         }
@@ -528,13 +540,18 @@ static hipError_t launch_p1(const ScoreArgs& a, size_t lds, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int KT>
-static hipError_t launch_p2(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  hipError_t e = allow_lds(score_pass2_kernel<T, D, KT>, lds);
+template <typename T, int D, int KT, bool MAX>
+static hipError_t launch_p2_agg(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  hipError_t e = allow_lds(score_pass2_kernel<T, D, KT, MAX>, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D, KT>::kThreads);
-  score_pass2_kernel<T, D, KT><<<grid, block, lds, s>>>(a);
+  score_pass2_kernel<T, D, KT, MAX><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int KT>
+static hipError_t launch_p2(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  return a.agg_max ? launch_p2_agg<T, D, KT, true>(a, lds, s) : launch_p2_agg<T, D, KT, false>(a, lds, s);
 }
 
 hipError_t launch_score_pass1(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s) {

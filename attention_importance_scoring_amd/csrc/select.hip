@@ -377,10 +377,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   if (unit >= a.n_units || t >= per_unit) return;
   const int row = (int)(t / vpr), col = (int)(t % vpr);
   const int src_row = a.idx ? a.idx[unit * a.n_rows + row] : row;
+  // source unit: same layer, head (unit % units_per_layer) / src_repeat
+  const int64_t src_unit = (unit / a.units_per_layer) * a.src_units_per_layer + (unit % a.units_per_layer) / a.src_repeat;
   char* dst = static_cast<char*>(a.dst) + unit * a.dst_unit_stride + (int64_t)row * a.row_bytes + col * 16;
   u32x4 v = {0u, 0u, 0u, 0u};
   if (src_row >= 0 && src_row < a.n_src_rows)
-    v = ldg16(static_cast<const char*>(a.src) + unit * a.src_unit_stride + (int64_t)src_row * a.row_bytes + col * 16);
+    v = ldg16(static_cast<const char*>(a.src) + src_unit * a.src_unit_stride + (int64_t)src_row * a.row_bytes + col * 16);
   *reinterpret_cast<u32x4*>(dst) = v;
 }
 

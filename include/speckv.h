@@ -56,6 +56,9 @@ typedef enum skv_dtype { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
 
 typedef enum skv_pool { SKV_POOL_NONE = 0, SKV_POOL_MAX = 1, SKV_POOL_AVG = 2 } skv_pool;
 
+/* Aggregation of the observation rows' probabilities into a key's score. */
+typedef enum skv_agg { SKV_AGG_SUM = 0, SKV_AGG_MAX = 1 } skv_agg;
+
 /* Problem shape.  Layouts (row-major, head_dim contiguous):
  *   K, V   : [n_layers][n_kv_heads][kv_head_stride]; head slab h of layer l
  *            holds n_in rows of head_dim elements, rows beyond n_in unused.
@@ -63,7 +66,12 @@ typedef enum skv_pool { SKV_POOL_NONE = 0, SKV_POOL_MAX = 1, SKV_POOL_AVG = 2 } 
  *            window rows first, then lookahead rows.
  *   SpecPC : Q_win [n_layers][n_q_heads][n_window][head_dim]; row i is the
  *            query of input position n_in - n_window + i.
- * Query head hq uses KV head hq / (n_q_heads / n_kv_heads). */
+ * Query head hq uses KV head hq / G, G = n_q_heads / n_kv_heads.
+ * SpecKV scores, selects and compacts per "head" h < H, where H = n_kv_heads
+ * (one kept set per KV head, shared by its G query heads; the default) or
+ * H = n_q_heads with per_query_head = 1 (the key designs paragraph scores
+ * "each attention head"; query head hq is scored alone against KV head
+ * hq / G, and its compacted cache holds rows of that KV head). */
 typedef struct skv_shape {
   int32_t n_layers;       /* >= 1                                                   */
   int32_t n_q_heads;      /* multiple of n_kv_heads                                 */
@@ -75,6 +83,8 @@ typedef struct skv_shape {
   int32_t n_lookahead;    /* SpecKV: draft rows (>= 0); SpecPC: 1                   */
   float scale;            /* logit scale; 0 means 1 / sqrt(head_dim)                */
   int32_t dtype;          /* skv_dtype of Q, K and V                                */
+  int32_t aggregation;    /* SpecKV: skv_agg over the observation rows; SpecPC: 0   */
+  int32_t per_query_head; /* SpecKV: 0 (H = n_kv_heads) or 1 (H = n_q_heads); SpecPC: 0 */
 } skv_shape;
 
 /* Human-readable name of a status code (static storage). */
@@ -90,13 +100,15 @@ skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t*
 skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out_n_keep);
 
 /* SpecKV importance scores ("Key designs", SpecKV).
- * For every layer l and KV head h, with rows r = (query head g of the group,
- * observation row i) and the n_pre = n_in - n_window remaining input keys:
+ * For every layer l and head h < H, with rows r = (query head g of h's
+ * group, or h's query head alone with per_query_head, and observation row
+ * i) and the n_pre = n_in - n_window remaining input keys:
  *   P[r][j]  = softmax over j < n_pre of scale * <q_r, k_j>
- *   score[j] = sum over r of P[r][j]
+ *   score[j] = sum over r of P[r][j]        (aggregation SKV_AGG_SUM)
+ *            = max over r of P[r][j]        (aggregation SKV_AGG_MAX)
  * Inputs : q_obs (see skv_shape), k.
- * Output : scores float [n_layers][n_kv_heads][n_pre] (raw sums; they total
- *          G * (n_window + n_lookahead) per head).
+ * Output : scores float [n_layers][H][n_pre] (raw sums total G or 1 times
+ *          (n_window + n_lookahead) per head).
  * Requires n_window + n_lookahead >= 1 and G * (n_window + n_lookahead)
  * <= 2^20; n_pre = 0 is accepted and does nothing. */
 skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
@@ -108,9 +120,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
  * in-range mean; SKV_POOL_NONE copies); then the min(C_max, n_pre) best
  * prefix keys, ordered by pooled score descending and lower index first on
  * ties, plus every window key n_pre .. n_in - 1; written ascending.
- * Inputs : scores float [n_layers][n_kv_heads][n_pre] (non-negative).
- * Outputs: kept int32 [n_layers][n_kv_heads][n_keep]; pooled float
- *          [n_layers][n_kv_heads][n_pre] or NULL.
+ * Inputs : scores float [n_layers][H][n_pre] (non-negative).
+ * Outputs: kept int32 [n_layers][H][n_keep]; pooled float
+ *          [n_layers][H][n_pre] or NULL.
  * The SpecPC token selection is this call on a shape with n_layers = 1,
  * n_kv_heads = 1 (n_q_heads = 1), n_in = tokens, n_window = 0. */
 skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool,
@@ -118,13 +130,15 @@ skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_
                          size_t workspace_bytes, void* stream);
 
 /* SpecKV compaction ("Key designs", SpecKV: keep the selected KV pairs).
- * Per head: out[t] = in[kept[t]] for t < n_keep, for K and V, bit-exact.
- * Out of place: k_out, v_out are [n_layers][n_kv_heads][n_keep][head_dim]
- *   and must not overlap k or v.
+ * Per head h < H: out[t] = in[kept[t]] for t < n_keep, for K and V,
+ * bit-exact, reading KV head h (or h / G with per_query_head).
+ * Out of place: k_out, v_out are [n_layers][H][n_keep][head_dim] and must
+ *   not overlap k or v.
  * In place: k_out == k and v_out == v; rows 0 .. n_keep - 1 of every head
  *   slab are overwritten, the stride is unchanged and rows >= n_keep are
- *   left unspecified.  Requires kept ascending (as speckv_select writes it).
- * kept values must lie in [0, n_in); n_keep in 1 .. n_in. */
+ *   left unspecified.  Requires kept ascending (as speckv_select writes it),
+ *   and H = n_kv_heads (SKV_ERR_PARAM otherwise).
+ * kept int32 [n_layers][H][n_keep], values in [0, n_in); n_keep in 1 .. n_in. */
 skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, const int32_t* kept,
                           int64_t n_keep, void* k_out, void* v_out, void* workspace,
                           size_t workspace_bytes, void* stream);
@@ -139,7 +153,8 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
  * (1 at the end of the window, 0.1 at its far edge; 1 when W = 1).
  * Inputs : q_win [n_layers][n_q_heads][W][head_dim] (all layers, skipped
  *          ones included), k.  Output: token_scores float [n_in].
- * Requires 0 <= l_skip < n_layers, 1 <= W <= n_in and G * W <= 2^20. */
+ * Requires 0 <= l_skip < n_layers, 1 <= W <= n_in, G * W <= 2^20, and
+ * aggregation = per_query_head = 0 (SKV_ERR_PARAM otherwise). */
 skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,
                                const float* query_weights, float* token_scores, void* workspace,
                                size_t workspace_bytes, void* stream);

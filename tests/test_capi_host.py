@@ -69,6 +69,8 @@ def _ws_bytes(lib, s, C_max=64):
     (dict(kv_head_stride=1000 * 128 - 8), SHAPE),
     (dict(kv_head_stride=1000 * 128 + 4), ALIGN),
     (dict(scale=-1.0), PARAM),
+    (dict(aggregation=2), PARAM),
+    (dict(per_query_head=2), PARAM),
 ])
 def test_shape_validation(lib, kw, status):
     s = shape(**kw)
@@ -169,3 +171,22 @@ def test_profile_interface_on_host(lib):
     assert lib.speckv_profile_count() == 0
     assert lib.speckv_profile_read(0, None, None, None) == PARAM
     assert lib.speckv_profile_enable(0) == OK
+
+
+def test_per_query_head_and_max_aggregation_rules(lib):
+    # one kept set per query head: 4x the units of the KV-head default (G = 4)
+    s, spq = shape(), shape(per_query_head=1, aggregation=skv.SKV_AGG_MAX)
+    st, base = _ws_bytes(lib, s, 64)
+    st2, per_q = _ws_bytes(lib, spq, 64)
+    assert st == OK and st2 == OK and per_q >= 2 * 8 * 984 * 4 and per_q > base
+    # a per-query-head cache does not fit the KV slabs: in-place compaction is refused
+    k, v, kept, ws = P(1 << 30), P(2 << 30), P(3 << 30), P(6 << 30)
+    assert lib.speckv_compact(ctypes.byref(spq), k, v, kept, 80, k, v, ws, 1 << 30, None) == PARAM
+    # ... unless every query head is its own KV head
+    s1 = shape(n_q_heads=2, per_query_head=1)
+    assert lib.speckv_compact(ctypes.byref(s1), k, v, kept, 80, k, v, None, 0, None) == WS
+    # SpecPC has its own aggregation: both fields must stay 0
+    for kw in (dict(aggregation=1), dict(per_query_head=1)):
+        sp = shape(**kw)
+        assert lib.specpc_token_scores(ctypes.byref(sp), 0, P(256), P(512), None, P(1024), P(4096), 1 << 30,
+                                       None) == PARAM

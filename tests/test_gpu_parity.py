@@ -154,6 +154,42 @@ def test_logit_jumps_between_key_groups(late):
     np.testing.assert_allclose(got.sum(-1), cfg.G * cfg.n_obs, rtol=1e-4)
 
 
+@pytest.mark.parametrize("agg,pqh", [("max", False), ("sum", True), ("max", True)],
+                         ids=["max-per-kv-head", "sum-per-query-head", "max-per-query-head"])
+def test_aggregation_and_per_query_head_variants(agg, pqh):
+    # G * n_obs = 520 rows: two row parts per KV head, so the max aggregation
+    # also crosses the part combine.
+    cfg = wl.reduced(wl.CONFIGS[2], n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=3000, n_window=40, n_lookahead=90,
+                     C_max=150)
+    print(f"\n[case] aggregation {agg}, per_query_head {pqh}", flush=True)
+    host = wl.speckv_inputs(cfg, 17, "cpu")
+    inp = _to(host, "cuda")
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    H, rep = (Hq, Hq // Hkv) if pqh else (Hkv, 1)
+    shape = skv.make_shape(L, Hq, Hkv, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, skv.SKV_BF16,
+                           kv_head_stride=inp["kv_head_stride"],
+                           aggregation=skv.SKV_AGG_MAX if agg == "max" else skv.SKV_AGG_SUM, per_query_head=int(pqh))
+    ws = workspace(shape, cfg.C_max)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    scores = torch.full((L, H, cfg.n_pre), float("nan"), dtype=torch.float32, device="cuda")
+    pooled = torch.full_like(scores, float("nan"))
+    kept = torch.full((L, H, n_keep), -1, dtype=torch.int32, device="cuda")
+    kc = torch.empty((L, H, n_keep, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], scores, ws)
+    skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws)
+    skv.speckv_compact(shape, inp["k_buf"], inp["v_buf"], kept, n_keep, kc, vc, ws)
+    torch.cuda.synchronize()
+    want = oracle.speckv_scores(np64(host["q_obs"]), np64(host["k"]), cfg.n_window, aggregation=agg,
+                                per_query_head=pqh)
+    got = scores.cpu().numpy()
+    assert_scores_close(got, want, cfg.G, cfg.n_obs)
+    pooled_o = oracle.pool1d(want, cfg.pool_kernel, "max")
+    assert_kept_matches(kept.cpu().numpy().reshape(L * H, -1), pooled.cpu().numpy().reshape(L * H, -1),
+                        pooled_o.reshape(L * H, -1), cfg.C_max, cfg.n_window)
+    assert_compacted(kc, vc, inp["k"].repeat_interleave(rep, dim=1), inp["v"].repeat_interleave(rep, dim=1), kept)
+
+
 def test_in_place_equals_out_of_place_and_deterministic():
     cfg = wl.reduced(wl.CONFIGS[4], n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
     host = wl.speckv_inputs(cfg, 7, "cpu")
