@@ -36,6 +36,10 @@ def parse():
     p.add_argument("--workload", default="qwen32b_shape_64k",
                    choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--aggregation", choices=["sum", "max"], default="sum",
+                   help="SpecKV: aggregate the observation rows' probabilities by sum (default) or max")
+    p.add_argument("--per-query-head", action="store_true",
+                   help="SpecKV: one kept set (and compacted cache) per query head instead of per KV head")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
     p.add_argument("--seed", type=int, default=0)
@@ -113,11 +117,16 @@ def bench_speckv(args, cfg, torch, skv, wl):
     inp = wl.speckv_inputs(cfg, seed=args.seed or 3, device=dev, layers=from_layers)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
-    L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    L, Hkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    H = cfg.n_q_heads if args.per_query_head else Hkv  # heads that get their own kept set
     dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
     per_layer = cfg.in_place  # the in-place workload keeps one layer's cache per call
+    if per_layer and args.per_query_head:
+        raise SystemExit("per-query-head caches are compacted out of place; the in-place workload does not take it")
     call_layers = 1 if per_layer else L
-    shape = skv.make_shape(call_layers, cfg.n_q_heads, H, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, dt)
+    shape = skv.make_shape(call_layers, cfg.n_q_heads, Hkv, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, dt,
+                           aggregation=skv.SKV_AGG_MAX if args.aggregation == "max" else skv.SKV_AGG_SUM,
+                           per_query_head=int(args.per_query_head))
     ws = torch.empty(skv.speckv_workspace_bytes(shape, cfg.C_max), dtype=torch.uint8, device=dev)
     n_keep = skv.speckv_n_keep(shape, cfg.C_max)
     scores = torch.empty((L, H, cfg.n_pre), dtype=torch.float32, device=dev)
@@ -159,9 +168,9 @@ def bench_speckv(args, cfg, torch, skv, wl):
     skv.profile_enable(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    keys = cfg.keys_per_call
-    R = cfg.G * cfg.n_obs
-    flops_per_pass = 2.0 * R * cfg.n_pre * d * L * H   # one Q_obs K^T over every head
+    keys = cfg.keys_per_call  # KV pairs scored and compacted (each query head's copy counted once)
+    flops_per_pass = 2.0 * cfg.n_obs * cfg.n_q_heads * L * cfg.n_pre * d  # one Q_obs K^T over every head
+    default_variant = args.aggregation == "sum" and not args.per_query_head
     kern = {name: {"launches": n, "avg_ms": t / max(n, 1), "ms_per_step": t / args.steps} for name, (n, t) in prof.items()}
     # dominant kernel: the longer of the two scoring passes (each computes one Q_obs K^T)
     dom = max(("score_pass1", "score_pass2"), key=lambda k: kern[k]["ms_per_step"])
@@ -171,16 +180,17 @@ def bench_speckv(args, cfg, torch, skv, wl):
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = flops_per_launch / avg_s / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name)}
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name) if default_variant else None}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
     path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
     out = {
         "metric": METRIC, "value": keys / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "n_layers": L, "n_q_heads": cfg.n_q_heads, "n_kv_heads": H, "head_dim": d,
+        "config": {"workload": cfg.name, "n_layers": L, "n_q_heads": cfg.n_q_heads, "n_kv_heads": Hkv, "head_dim": d,
                    "n_in": cfg.n_in, "n_window": cfg.n_window, "n_lookahead": cfg.n_lookahead, "C_max": cfg.C_max,
-                   "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys},
+                   "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys,
+                   "aggregation": args.aggregation, "per_query_head": bool(args.per_query_head)},
         "roofline": roof,
         "path_mfma_frac": round(path_frac, 4),
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "ms_per_step": round(v["ms_per_step"], 4)}
