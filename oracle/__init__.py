@@ -6,8 +6,8 @@ its Python binding never import, link or call anything in here, and this
 package imports nothing from the library: the two share no code.
 
 Every function follows the text of the paper notes "Draft-based Approximate
-Inference for LLMs" (ICLR 2026 notes page, section "Key designs": the SpecKV
-and SpecPC paragraphs; section "Loss / training strategy": local pooling).
+Inference for LLMs" (ICLR 2026 notes page, section "Key designs": the SpecKV,
+SpecPC and SpecKV-PC paragraphs; section "Loss / training strategy": local pooling).
 Where the pages leave a step open, the reading taken is stated in the
 function's docstring under "Reading".
 
@@ -35,3 +35,4 @@ from .specpc import (  # noqa: F401
     specpc_select,
 )
 from .theorem1 import pre_softmax_scores, theorem1_bound  # noqa: F401
+from .cascade import gather_tokens, speckv_pc_cascade  # noqa: F401
