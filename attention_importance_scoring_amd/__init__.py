@@ -15,7 +15,7 @@ from ._lib import SKV_AGG_MAX, SKV_AGG_SUM, SKV_BF16, SKV_F32, SKV_POOL_AVG, SKV
 
 __all__ = [
     "Shape", "SpecKVError", "make_shape", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores",
-    "speckv_select", "speckv_compact", "specpc_token_scores", "profile_enable", "profile_read",
+    "speckv_select", "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "profile_enable", "profile_read",
     "SKV_F32", "SKV_BF16", "SKV_POOL_NONE", "SKV_POOL_MAX", "SKV_POOL_AVG", "SKV_AGG_SUM", "SKV_AGG_MAX",
 ]
 
@@ -89,6 +89,12 @@ def speckv_compact(shape: Shape, k, v, kept, n_keep: int, k_out, v_out, workspac
     _check(_lib.load().speckv_compact(ctypes.byref(shape), _ptr(k, "k"), _ptr(v, "v"), _ptr(kept, "kept"), n_keep,
                                       _ptr(k_out, "k_out"), _ptr(v_out, "v_out"), w, wb, _stream(stream)),
            "speckv_compact")
+
+
+def specpc_gather_tokens(shape: Shape, k, v, tokens, n_tokens: int, k_out, v_out, stream=None):
+    _check(_lib.load().specpc_gather_tokens(ctypes.byref(shape), _ptr(k, "k"), _ptr(v, "v"), _ptr(tokens, "tokens"),
+                                            n_tokens, _ptr(k_out, "k_out"), _ptr(v_out, "v_out"), _stream(stream)),
+           "specpc_gather_tokens")
 
 
 def specpc_token_scores(shape: Shape, l_skip: int, q_win, k, query_weights, token_scores, workspace, stream=None):

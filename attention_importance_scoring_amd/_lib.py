@@ -23,7 +23,7 @@ SKV_AGG_SUM, SKV_AGG_MAX = 0, 1
 # Every symbol include/speckv.h declares.
 EXPORTED = (
     "speckv_status_string", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores", "speckv_select",
-    "speckv_compact", "specpc_token_scores", "speckv_profile_enable", "speckv_profile_count", "speckv_profile_read",
+    "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "speckv_profile_enable", "speckv_profile_count", "speckv_profile_read",
 )
 
 
@@ -64,6 +64,8 @@ def load(path: str | None = None):
     lib.speckv_compact.restype = c_int32
     lib.speckv_compact.argtypes = [S, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t,
                                    c_void_p]
+    lib.specpc_gather_tokens.restype = c_int32
+    lib.specpc_gather_tokens.argtypes = [S, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]
     lib.specpc_token_scores.restype = c_int32
     lib.specpc_token_scores.argtypes = [S, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]

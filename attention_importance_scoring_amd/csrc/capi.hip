@@ -361,6 +361,7 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
       return SKV_ERR_ALIAS;
     ProfScope p("compact_gather", s);
     g.idx = kept;
+    g.idx_unit_stride = n_keep;
     g.dst_unit_stride = n_keep * row_bytes;
     g.src = k;
     g.dst = k_out;
@@ -382,6 +383,7 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
   {
     ProfScope p("compact_gather", s);
     g.idx = kept;
+    g.idx_unit_stride = n_keep;
     g.dst_unit_stride = n_keep * row_bytes;
     g.src = k;
     g.dst = ks;
@@ -407,6 +409,44 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
   b.src = vs;
   b.dst = const_cast<void*>(v);
   return hip_status(launch_gather(b, s));
+}
+
+skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const void* v, const int32_t* tokens,
+                                int64_t n_tokens, void* k_out, void* v_out, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!k || !v || !tokens || !k_out || !v_out) return SKV_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > d.n_in) return SKV_ERR_PARAM;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(tokens, 4))
+    return SKV_ERR_ALIGN;
+  const int64_t units = d.L * d.Hkv, row_bytes = d.D * d.esize;
+  const size_t in_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * row_bytes);
+  const size_t out_bytes = (size_t)(units * n_tokens * row_bytes);
+  const size_t tok_bytes = (size_t)n_tokens * 4;
+  if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+      ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
+      ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(tokens, tok_bytes, k_out, out_bytes) ||
+      ranges_overlap(tokens, tok_bytes, v_out, out_bytes))
+    return SKV_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GatherArgs g{};
+  g.n_units = (int32_t)units;
+  g.units_per_layer = g.src_units_per_layer = (int32_t)d.Hkv;
+  g.src_repeat = 1;
+  g.n_rows = (int32_t)n_tokens;
+  g.n_src_rows = (int32_t)d.n_in;
+  g.row_bytes = (int32_t)row_bytes;
+  g.src_unit_stride = d.stride * d.esize;
+  g.dst_unit_stride = n_tokens * row_bytes;
+  g.idx = tokens;
+  g.idx_unit_stride = 0;  // one token list for every (layer, KV head)
+  ProfScope p("gather_tokens", s);
+  g.src = k;
+  g.dst = k_out;
+  SKV_TRY(hip_status(launch_gather(g, s)));
+  g.src = v;
+  g.dst = v_out;
+  return hip_status(launch_gather(g, s));
 }
 
 skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,

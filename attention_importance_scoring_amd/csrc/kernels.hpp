@@ -89,11 +89,12 @@ int select_segments(int64_t n_units, int64_t n_pre, int64_t n_top);
 size_t select_candidate_bytes(int64_t n_units, int64_t n_pre, int64_t n_top);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
-// Row gather: dst[u][t] = src[u][idx[u][t]] (or src[u][t] when idx is null).
+// Row gather: dst[u][t] = src[u][idx[u * idx_unit_stride + t]] (or src[u][t] when idx is null).
 struct GatherArgs {
   const void* src;
   void* dst;
-  const int32_t* idx;       // [n_units][n_rows] or nullptr
+  const int32_t* idx;       // per-unit lists (idx_unit_stride = n_rows), one shared list (0), or nullptr
+  int64_t idx_unit_stride;  // elements
   int64_t src_unit_stride;  // bytes
   int64_t dst_unit_stride;  // bytes
   int32_t n_units;          // destination units

@@ -21,6 +21,10 @@ synthetic key distributions below:
 * "mixture": 90% N(0, I) keys, 10% (random positions) drawn as c_m + 0.1 N(0, I)
   around 64 random centroids c_m ~ N(0, I) per head.
 
+The SpecKV-PC cascade (section "Key designs", SpecKV-PC) pairs the draft
+workload with a Qwen2.5-32B-shaped target cache over the same 32K prompt;
+SpecPC keeps 2048 tokens and SpecKV then keeps 256 pairs per KV head.
+
 Everything is drawn in fp32 and rounded once to the storage dtype
 (round-to-nearest-even for bf16).
 """
@@ -107,6 +111,30 @@ CONFIGS = {
     4: SpecKVConfig("llama8b_shape_128k_inplace", 32, 32, 8, 128, "bf16", 131072, 64, 256, 2048, 7, "mixture", "none", 0.0,
                     in_place=True),
     5: SpecPCConfig("specpc_draft_32k", 24, 14, 2, 64, "bf16", 32768, 512, 1, 4, 2048, 7, 2.5),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class CascadeConfig:
+    """SpecKV-PC: SpecPC keeps draft.k_top of the draft.n_in prompt tokens,
+    then SpecKV runs on the target's cache over those tokens.  `target`
+    describes the target cache over the FULL prompt (n_in = draft.n_in); its
+    rows at the kept tokens stand in for the target's prefill of the
+    compressed prompt.  `stage2` is the SpecKV shape over the kept tokens."""
+    name: str
+    draft: SpecPCConfig
+    target: SpecKVConfig
+
+    @property
+    def stage2(self) -> SpecKVConfig:
+        return dataclasses.replace(self.target, name=self.name + "_stage2", n_in=self.draft.k_top)
+
+
+CASCADES = {
+    "speckv_pc_cascade_32k": CascadeConfig(
+        "speckv_pc_cascade_32k", CONFIGS[5],
+        SpecKVConfig("qwen32b_shape_32k_target", 64, 40, 8, 128, "bf16", 32768, 32, 128, 256, 7, "lowrank8",
+                     "one_percent", 2.5)),
 }
 
 _TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "hh": 4, "lowrank": 5, "mix": 6}
@@ -222,6 +250,14 @@ def specpc_inputs(cfg: SpecPCConfig, seed: int, device="cpu"):
     for layer in range(L):
         q_win[layer], k[layer] = specpc_layer(cfg, layer, seed, device)
     return {"q_win": q_win, "k": k}
+
+
+def cascade_inputs(cc: CascadeConfig, seed: int, device="cpu", target_layers=None):
+    """Draft inputs (seed) and the target's full-prompt cache and observation
+    queries (seed + 1): {"draft": specpc_inputs(...), "target": speckv_inputs(...)}.
+    The draft's and the target's planted keys are drawn independently."""
+    return {"draft": specpc_inputs(cc.draft, seed, device),
+            "target": speckv_inputs(cc.target, seed + 1, device, layers=target_layers)}
 
 
 def reduced(cfg, **changes):

@@ -34,7 +34,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen32b_shape_64k",
-                   choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k"])
+                   choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k",
+                            "speckv_pc_cascade_32k"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--aggregation", choices=["sum", "max"], default="sum",
                    help="SpecKV: aggregate the observation rows' probabilities by sum (default) or max")
@@ -245,6 +246,80 @@ def bench_specpc(args, cfg, torch, skv, wl):
     }, inp
 
 
+def bench_cascade(args, cc, torch, skv, wl):
+    """SpecKV-PC: SpecPC token scores + selection on the draft stack, the
+    target cache gathered at the kept tokens, then SpecKV scores, selection
+    and compaction over the compressed prompt, all on one stream."""
+    dev = "cuda"
+    inp = wl.cascade_inputs(cc, seed=args.seed or 5, device=dev)
+    torch.cuda.synchronize()
+    dr, st2, tg = cc.draft, cc.stage2, inp["target"]
+    dt = skv.SKV_F32 if dr.dtype == "f32" else skv.SKV_BF16
+    pc_shape = skv.make_shape(dr.n_layers, dr.n_q_heads, dr.n_kv_heads, dr.head_dim, dr.n_in, dr.window,
+                              dr.n_lookahead, dt)
+    sel_shape = skv.make_shape(1, 1, 1, dr.head_dim, dr.n_in, 0, 0, dt)
+    full_shape = skv.make_shape(cc.target.n_layers, cc.target.n_q_heads, cc.target.n_kv_heads, cc.target.head_dim,
+                                cc.target.n_in, cc.target.n_window, cc.target.n_lookahead, skv.SKV_BF16,
+                                kv_head_stride=tg["kv_head_stride"])
+    s2_shape = skv.make_shape(st2.n_layers, st2.n_q_heads, st2.n_kv_heads, st2.head_dim, st2.n_in, st2.n_window,
+                              st2.n_lookahead, skv.SKV_BF16)
+    ws = torch.empty(skv.speckv_workspace_bytes(pc_shape, dr.k_top), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(skv.speckv_workspace_bytes(s2_shape, st2.C_max), dtype=torch.uint8, device=dev)
+    L, H, d, n_tok = st2.n_layers, st2.n_kv_heads, st2.head_dim, dr.k_top
+    ts = torch.empty(dr.n_in, dtype=torch.float32, device=dev)
+    ts_pooled = torch.empty_like(ts)
+    tokens = torch.empty(n_tok, dtype=torch.int32, device=dev)
+    k_tok = torch.empty((L, H, n_tok, d), dtype=tg["k"].dtype, device=dev)
+    v_tok = torch.empty_like(k_tok)
+    n_keep = skv.speckv_n_keep(s2_shape, st2.C_max)
+    scores = torch.empty((L, H, st2.n_pre), dtype=torch.float32, device=dev)
+    pooled = torch.empty_like(scores)
+    kept = torch.empty((L, H, n_keep), dtype=torch.int32, device=dev)
+    kc = torch.empty((L, H, n_keep, d), dtype=tg["k"].dtype, device=dev)
+    vc = torch.empty_like(kc)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        skv.specpc_token_scores(pc_shape, dr.l_skip, inp["draft"]["q_win"], inp["draft"]["k"], None, ts, ws, stream)
+        skv.speckv_select(sel_shape, ts, dr.k_top, skv.SKV_POOL_MAX, dr.pool_kernel, tokens, ts_pooled, ws, stream)
+        skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
+        skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
+        skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
+        skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    skv.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = skv.profile_read()
+    skv.profile_enable(False)
+    kern = {name: {"launches": n, "avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
+            for name, (n, t) in prof.items()}
+    # the gather moves n_tok rows of K and V per (layer, KV head) in and out
+    g = kern.get("gather_tokens")
+    gather_bytes = 2 * 2 * L * H * n_tok * d * 2  # K and V, read and write, bf16
+    gather_gbs = gather_bytes / (g["ms_per_step"] * 1e-3) / 1e9 if g else None
+    return {
+        "metric": "SpecKV-PC cascade: prompt tokens compressed/sec (SpecPC to k_top tokens, SpecKV to C_max pairs)",
+        "value": dr.n_in / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dr.dtype, "data": "synthetic",
+        "config": {"workload": cc.name, "n_in": dr.n_in, "draft_layers": dr.n_layers, "l_skip": dr.l_skip,
+                   "draft_heads": [dr.n_q_heads, dr.n_kv_heads, dr.head_dim], "window": dr.window, "k_top": n_tok,
+                   "target_layers": L, "target_heads": [st2.n_q_heads, H, d], "n_window": st2.n_window,
+                   "n_lookahead": st2.n_lookahead, "C_max": st2.C_max},
+        "gather_tokens_GBps": round(gather_gbs, 1) if gather_gbs else None,
+        "kernels": kern,
+    }, inp
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -259,6 +334,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload in wl.CASCADES:
+        out, _ = bench_cascade(args, wl.CASCADES[args.workload], torch, skv, wl)
+        print(json.dumps(out), flush=True)
+        return
     cfg = {c.name: c for c in wl.CONFIGS.values()}[args.workload]
     if args.workload == "specpc_draft_32k":
         out, inp = bench_specpc(args, cfg, torch, skv, wl)

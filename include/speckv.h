@@ -143,6 +143,24 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
                           int64_t n_keep, void* k_out, void* v_out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Token gather for the SpecKV-PC cascade ("Key designs", SpecKV-PC: SpecPC
+ * first cuts the prompt to its kept tokens, then SpecKV works on the
+ * target's cache over that shorter prompt).  For every layer and KV head:
+ *   k_out[t] = k[tokens[t]], v_out[t] = v[tokens[t]] for t < n_tokens,
+ * bit-exact, with one token list shared by every head (as specpc_token_scores
+ * and speckv_select produce it).  It stands in for the target's cache of the
+ * compressed prompt when a cache over the full prompt is at hand.
+ * Uses n_layers, n_kv_heads, head_dim, n_in, kv_head_stride and dtype of
+ * the shape (the rest is validated as usual and otherwise ignored).
+ * Inputs : k, v [n_layers][n_kv_heads][kv_head_stride] (rows of n_in);
+ *          tokens int32 [n_tokens] on the device, values in [0, n_in) (a
+ *          token outside that range yields a zero row).
+ * Outputs: k_out, v_out [n_layers][n_kv_heads][n_tokens][head_dim],
+ *          contiguous; out of place only (SKV_ERR_ALIAS on any overlap).
+ * Requires 1 <= n_tokens <= n_in (SKV_ERR_PARAM otherwise). */
+skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const void* v, const int32_t* tokens,
+                                int64_t n_tokens, void* k_out, void* v_out, void* stream);
+
 /* SpecPC token scores ("Key designs", SpecPC).
  * For layers l_skip <= l < n_layers and every query head hq, window row i
  * (position p_i = n_in - W + i, W = n_window) attends causally:

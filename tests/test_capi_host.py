@@ -190,3 +190,20 @@ def test_per_query_head_and_max_aggregation_rules(lib):
         sp = shape(**kw)
         assert lib.specpc_token_scores(ctypes.byref(sp), 0, P(256), P(512), None, P(1024), P(4096), 1 << 30,
                                        None) == PARAM
+
+
+def test_gather_tokens_validation(lib):
+    s = shape()  # 2 layers x 2 KV heads x 1000 rows x 128 bf16: 256 KB per head slab
+    k, v, tok, ko, vo = P(1 << 30), P(2 << 30), P(3 << 30), P(4 << 30), P(5 << 30)
+    g = lambda *a: lib.specpc_gather_tokens(ctypes.byref(s), *a, None)
+    assert g(k, v, tok, 0, ko, vo) == PARAM
+    assert g(k, v, tok, 1001, ko, vo) == PARAM
+    assert g(None, v, tok, 10, ko, vo) == NULL and g(k, v, None, 10, ko, vo) == NULL
+    assert g(k, v, tok, 10, k, v) == ALIAS                          # no in-place form
+    assert g(k, k, tok, 10, ko, vo) == ALIAS
+    assert g(k, v, tok, 10, P((2 << 30) + 1024 * 256), vo) == ALIAS  # K out inside V
+    assert g(k, v, tok, 10, ko, P((4 << 30) + 256)) == ALIAS        # K out and V out overlap
+    assert g(k, v, P((4 << 30) + 64), 10, ko, vo) == ALIAS          # token list inside K out
+    assert g(P((1 << 30) + 8), v, tok, 10, ko, vo) == ALIGN
+    assert g(k, v, P((3 << 30) + 2), 10, ko, vo) == ALIGN
+    assert lib.specpc_gather_tokens(None, k, v, tok, 10, ko, vo, None) == NULL

@@ -1,0 +1,127 @@
+"""GPU parity of the SpecKV-PC cascade through the C ABI: SpecPC token
+scores and selection on the draft stack, the target cache gathered at the
+kept tokens, then SpecKV scores, selection and compaction on the compressed
+prompt (paper notes "Draft-based Approximate Inference for LLMs", section
+"Key designs", SpecKV-PC paragraph).
+
+Each stage is compared with the oracle on the GPU's own input to that stage
+(the token list the GPU kept), under the same tolerances as the single-stage
+tests: scores within 1e-3 relative, selections equal to the rule on the
+GPU's own pooled scores and equal to the oracle's except at ties with the
+cut-off, gathered and compacted rows bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_importance_scoring_amd as skv
+import oracle
+from attention_importance_scoring_amd import workloads as wl
+
+from gpu_helpers import assert_kept_matches, assert_scores_close, np64, shape_of, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def run_cascade(cc, inp, stream=None):
+    """SpecPC -> select -> gather -> SpecKV scores -> select -> compact, one stream."""
+    dr, st2 = cc.draft, cc.stage2
+    dq, dk = inp["draft"]["q_win"], inp["draft"]["k"]
+    tg = inp["target"]
+    dev = dq.device
+    dt = skv.SKV_BF16 if dr.dtype == "bf16" else skv.SKV_F32
+    pc_shape = skv.make_shape(dr.n_layers, dr.n_q_heads, dr.n_kv_heads, dr.head_dim, dr.n_in, dr.window,
+                              dr.n_lookahead, dt)
+    sel_shape = skv.make_shape(1, 1, 1, dr.head_dim, dr.n_in, 0, 0, dt)
+    full_shape = shape_of(cc.target, kv_head_stride=tg["kv_head_stride"], n_layers=tg["q_obs"].shape[0])
+    L = tg["q_obs"].shape[0]
+    s2_shape = shape_of(st2, n_layers=L)
+    ws = workspace(pc_shape, dr.k_top)
+    ws2 = workspace(s2_shape, st2.C_max)
+    ts = torch.full((dr.n_in,), float("nan"), dtype=torch.float32, device=dev)
+    ts_pooled = torch.full_like(ts, float("nan"))
+    tokens = torch.full((dr.k_top,), -1, dtype=torch.int32, device=dev)
+    H, d, n_tok = st2.n_kv_heads, st2.head_dim, dr.k_top
+    k_tok = torch.empty((L, H, n_tok, d), dtype=tg["k"].dtype, device=dev)
+    v_tok = torch.empty_like(k_tok)
+    n_keep = skv.speckv_n_keep(s2_shape, st2.C_max)
+    scores = torch.full((L, H, st2.n_pre), float("nan"), dtype=torch.float32, device=dev)
+    pooled = torch.full_like(scores, float("nan"))
+    kept = torch.full((L, H, n_keep), -1, dtype=torch.int32, device=dev)
+    kc = torch.empty((L, H, n_keep, d), dtype=tg["k"].dtype, device=dev)
+    vc = torch.empty_like(kc)
+    skv.specpc_token_scores(pc_shape, dr.l_skip, dq, dk, None, ts, ws, stream)
+    skv.speckv_select(sel_shape, ts, dr.k_top, skv.SKV_POOL_MAX, dr.pool_kernel, tokens, ts_pooled, ws, stream)
+    skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
+    skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
+    skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
+    skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
+    return {"ts": ts, "ts_pooled": ts_pooled, "tokens": tokens, "k_tok": k_tok, "v_tok": v_tok, "scores": scores,
+            "pooled": pooled, "kept": kept, "k": kc, "v": vc}
+
+
+def _check_stage2(out, inp, cc, units):
+    """Stage 2 against the oracle on the GPU's own token list, for the given (layer, head) units."""
+    st2 = cc.stage2
+    tg = inp["target"]
+    tokens = out["tokens"].cpu().numpy().astype(np.int64)
+    tok_dev = torch.as_tensor(tokens, device=tg["k"].device)
+    assert torch.equal(out["k_tok"], tg["k"][:, :, tok_dev]), "gathered K differs from the target rows"
+    assert torch.equal(out["v_tok"], tg["v"][:, :, tok_dev]), "gathered V differs from the target rows"
+    sc, pl, kp = out["scores"].cpu().numpy(), out["pooled"].cpu().numpy(), out["kept"].cpu().numpy()
+    G, scale = st2.G, oracle.default_scale(st2.head_dim)
+    for layer, h in units:
+        k_c = oracle.gather_tokens(np64(tg["k"][layer:layer + 1, h:h + 1]), tokens)[0, 0]
+        want = oracle.head_scores(np64(tg["q_obs"][layer, h * G:(h + 1) * G]), k_c[:st2.n_pre], scale)
+        assert_scores_close(sc[layer, h], want, G, st2.n_obs, f"stage-2 scores[{layer},{h}]")
+        assert_kept_matches(kp[layer, h][None], pl[layer, h][None], oracle.pool1d(want, st2.pool_kernel, "max")[None],
+                            st2.C_max, st2.n_window, f"stage-2 kept[{layer},{h}]")
+    # every unit: invariants and bit-exact final cache at the original positions
+    positions = torch.as_tensor(tokens, device=tg["k"].device)[out["kept"].long()]
+    idx = positions.unsqueeze(-1).expand(*positions.shape, st2.head_dim)
+    assert torch.equal(out["k"], torch.gather(tg["k"], 2, idx)), "final K differs from the target rows"
+    assert torch.equal(out["v"], torch.gather(tg["v"], 2, idx)), "final V differs from the target rows"
+    pos = positions.cpu().numpy()
+    assert (np.diff(pos, axis=-1) > 0).all()
+    assert (pos[..., -st2.n_window:] == tokens[-st2.n_window:]).all()
+    np.testing.assert_allclose(sc.astype(np.float64).sum(-1), G * st2.n_obs, rtol=1e-4)
+
+
+def test_cascade_small_against_oracle():
+    base = wl.CASCADES["speckv_pc_cascade_32k"]
+    cc = wl.CascadeConfig("cascade_small",
+                          wl.reduced(base.draft, n_layers=6, l_skip=2, n_in=3000, window=128, k_top=400),
+                          wl.reduced(base.target, n_layers=3, n_in=3000, n_lookahead=16, C_max=50))
+    print(f"\n[case] {cc.name}: draft n_in {cc.draft.n_in} k_top {cc.draft.k_top}, target "
+          f"{cc.target.n_layers} layers, C_max {cc.target.C_max}", flush=True)
+    inp = wl.cascade_inputs(cc, 11, "cuda")
+    out = run_cascade(cc, inp)
+    torch.cuda.synchronize()
+    dr = cc.draft
+    want_ts = oracle.specpc_token_scores(np64(inp["draft"]["q_win"]), np64(inp["draft"]["k"]), dr.l_skip)
+    assert_scores_close(out["ts"].cpu().numpy(), want_ts, dr.G, dr.window, "token scores")
+    assert_kept_matches(out["tokens"].cpu().numpy()[None], out["ts_pooled"].cpu().numpy()[None],
+                        oracle.pool1d(want_ts, dr.pool_kernel, "max")[None], dr.k_top, 0, "tokens")
+    units = [(layer, h) for layer in range(cc.target.n_layers) for h in range(cc.target.n_kv_heads)]
+    _check_stage2(out, inp, cc, units)
+    # when the GPU kept the oracle's tokens (no tie at the cut-off), the whole oracle cascade applies
+    ref = oracle.speckv_pc_cascade(np64(inp["draft"]["q_win"]), np64(inp["draft"]["k"]), dr.l_skip, dr.k_top,
+                                   np64(inp["target"]["q_obs"]), np64(inp["target"]["k"]),
+                                   np64(inp["target"]["v"]), cc.stage2.n_window, cc.stage2.C_max)
+    if np.array_equal(ref["tokens"], out["tokens"].cpu().numpy()):
+        assert_scores_close(out["scores"].cpu().numpy(), ref["scores"], cc.target.G, cc.target.n_obs,
+                            "cascade scores")
+
+
+def test_cascade_full_size_sampled():
+    cc = wl.CASCADES["speckv_pc_cascade_32k"]
+    print(f"\n[case] {cc.name}: draft {cc.draft.n_layers} layers n_in {cc.draft.n_in}, target "
+          f"{cc.target.n_layers} layers x {cc.target.n_kv_heads} KV heads, stage 2 n_in {cc.stage2.n_in}", flush=True)
+    inp = wl.cascade_inputs(cc, 5, "cuda")  # the inputs bench.py times
+    out = run_cascade(cc, inp)
+    torch.cuda.synchronize()
+    # token selection: the rule on the GPU's own pooled token scores (the scores themselves are
+    # checked against the oracle on the same draft stack by the full-size SpecPC test)
+    exact = oracle.select_kept(out["ts_pooled"].cpu().numpy().astype(np.float64), cc.draft.k_top, 0)
+    assert (out["tokens"].cpu().numpy() == exact).all()
+    _check_stage2(out, inp, cc, [(0, 0), (31, 4), (63, 7)])
