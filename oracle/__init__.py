@@ -6,8 +6,9 @@ its Python binding never import, link or call anything in here, and this
 package imports nothing from the library: the two share no code.
 
 Every function follows the text of the paper notes "Draft-based Approximate
-Inference for LLMs" (ICLR 2026 notes page, section "Key designs": the SpecKV,
-SpecPC and SpecKV-PC paragraphs; section "Loss / training strategy": local pooling).
+Inference for LLMs" (ICLR 2026 notes page, section "Background": attention
+and KV cache cost; section "Key designs": the SpecKV, SpecPC and SpecKV-PC
+paragraphs; section "Loss / training strategy": local pooling).
 Where the pages leave a step open, the reading taken is stated in the
 function's docstring under "Reading".
 
@@ -36,3 +37,4 @@ from .specpc import (  # noqa: F401
 )
 from .theorem1 import pre_softmax_scores, theorem1_bound  # noqa: F401
 from .cascade import gather_tokens, speckv_pc_cascade  # noqa: F401
+from .decode import decode_attention, error_scale, head_attention  # noqa: F401
