@@ -15,7 +15,8 @@ from ._lib import SKV_AGG_MAX, SKV_AGG_SUM, SKV_BF16, SKV_F32, SKV_POOL_AVG, SKV
 
 __all__ = [
     "Shape", "SpecKVError", "make_shape", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores",
-    "speckv_select", "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "profile_enable", "profile_read",
+    "speckv_select", "speckv_compact", "specpc_gather_tokens", "specpc_token_scores",
+    "speckv_decode_workspace_bytes", "speckv_decode_attention", "profile_enable", "profile_read",
     "SKV_F32", "SKV_BF16", "SKV_POOL_NONE", "SKV_POOL_MAX", "SKV_POOL_AVG", "SKV_AGG_SUM", "SKV_AGG_MAX",
 ]
 
@@ -102,6 +103,19 @@ def specpc_token_scores(shape: Shape, l_skip: int, q_win, k, query_weights, toke
     _check(_lib.load().specpc_token_scores(ctypes.byref(shape), l_skip, _ptr(q_win, "q_win"), _ptr(k, "k"),
                                            _ptr(query_weights, "query_weights"), _ptr(token_scores, "token_scores"),
                                            w, wb, _stream(stream)), "specpc_token_scores")
+
+
+def speckv_decode_workspace_bytes(shape: Shape, n_rows: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.load().speckv_decode_workspace_bytes(ctypes.byref(shape), n_rows, ctypes.byref(out)),
+           "speckv_decode_workspace_bytes")
+    return out.value
+
+
+def speckv_decode_attention(shape: Shape, n_rows: int, q, k, v, out, workspace, stream=None):
+    w, wb = _ws(workspace)
+    _check(_lib.load().speckv_decode_attention(ctypes.byref(shape), n_rows, _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
+                                               _ptr(out, "out"), w, wb, _stream(stream)), "speckv_decode_attention")
 
 
 def profile_enable(on: bool):

@@ -23,7 +23,8 @@ SKV_AGG_SUM, SKV_AGG_MAX = 0, 1
 # Every symbol include/speckv.h declares.
 EXPORTED = (
     "speckv_status_string", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores", "speckv_select",
-    "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "speckv_profile_enable", "speckv_profile_count", "speckv_profile_read",
+    "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "speckv_decode_workspace_bytes",
+    "speckv_decode_attention", "speckv_profile_enable", "speckv_profile_count", "speckv_profile_read",
 )
 
 
@@ -69,6 +70,11 @@ def load(path: str | None = None):
     lib.specpc_token_scores.restype = c_int32
     lib.specpc_token_scores.argtypes = [S, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]
+    lib.speckv_decode_workspace_bytes.restype = c_int32
+    lib.speckv_decode_workspace_bytes.argtypes = [S, c_int64, ctypes.POINTER(c_size_t)]
+    lib.speckv_decode_attention.restype = c_int32
+    lib.speckv_decode_attention.argtypes = [S, c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                            c_void_p]
     lib.speckv_profile_enable.restype = c_int32
     lib.speckv_profile_enable.argtypes = [c_int32]
     lib.speckv_profile_count.restype = c_int32

@@ -511,6 +511,68 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   return hip_status(launch_specpc_reduce(pa, s));
 }
 
+size_t decode_ws_bytes(const Dims& d, int64_t n_rows) {
+  const int64_t units = d.L * d.heads();
+  int32_t n_sub = 1, chunks = 1;
+  decode_plan(units, n_rows, &n_sub, &chunks);
+  if (chunks <= 1) return 0;
+  const int64_t slots = units * chunks * decode_max_group();
+  return round_up((size_t)slots * sizeof(float2)) + round_up((size_t)(slots * d.D) * sizeof(float));
+}
+
+skv_status speckv_decode_workspace_bytes(const skv_shape* shape, int64_t n_rows, size_t* out_bytes) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!out_bytes) return SKV_ERR_NULL;
+  if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
+  *out_bytes = decode_ws_bytes(d, n_rows);
+  return SKV_OK;
+}
+
+skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const void* q, const void* k,
+                                   const void* v, float* out, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (d.dtype != SKV_BF16) return SKV_ERR_DTYPE;
+  if (!q || !k || !v || !out) return SKV_ERR_NULL;
+  if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
+  if (d.group() > decode_max_group()) return SKV_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4)) return SKV_ERR_ALIGN;
+  const int64_t units = d.L * d.heads();
+  const size_t cache_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * d.D * d.esize);
+  const size_t out_bytes = (size_t)(d.L * d.Hq * d.D) * sizeof(float);
+  if (ranges_overlap(out, out_bytes, q, (size_t)(d.L * d.Hq * d.D * d.esize)) ||
+      ranges_overlap(out, out_bytes, k, cache_bytes) || ranges_overlap(out, out_bytes, v, cache_bytes))
+    return SKV_ERR_ALIAS;
+  const size_t need = decode_ws_bytes(d, n_rows);
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.head_stride = d.stride;
+  a.n_rows = n_rows;
+  a.n_units = (int32_t)units;
+  a.heads_per_layer = (int32_t)d.heads();
+  a.q_heads_per_layer = (int32_t)d.Hq;
+  a.group = (int32_t)d.group();
+  decode_plan(units, n_rows, &a.n_sub, &a.n_chunks);
+  a.c = d.scale * 1.4426950408889634f;
+  a.out = out;
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return SKV_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+    if (ranges_overlap(ws, need, out, out_bytes) || ranges_overlap(ws, need, k, cache_bytes) ||
+        ranges_overlap(ws, need, v, cache_bytes))
+      return SKV_ERR_ALIAS;
+    const int64_t slots = units * a.n_chunks * decode_max_group();
+    a.part_ml = static_cast<float2*>(ws);
+    a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)slots * sizeof(float2)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ProfScope p("decode_attention", s);
+  return hip_status(launch_decode_attention((int)d.D, a, s));
+}
+
 skv_status speckv_profile_enable(int32_t on) {
   if (on) {
     g_prof.clear();

@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen32b_shape_64k",
                    choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k",
-                            "speckv_pc_cascade_32k"])
+                            "speckv_pc_cascade_32k", "decode_qwen32b_shape_64k"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--aggregation", choices=["sum", "max"], default="sum",
                    help="SpecKV: aggregate the observation rows' probabilities by sum (default) or max")
@@ -320,6 +320,76 @@ def bench_cascade(args, cc, torch, skv, wl):
     }, inp
 
 
+def bench_decode(args, cfg, torch, skv, wl):
+    """Decode attention for one new token per query head, all layers in one
+    call, over the compacted cache that scores + select + compact produce
+    (n_keep rows per KV head) and, for comparison, over the full cache
+    (n_in rows).  The timed call is the compacted one; both are reported."""
+    dev = "cuda"
+    inp = wl.speckv_inputs(cfg, seed=args.seed or 3, device=dev)
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    shape = skv.make_shape(L, Hq, Hkv, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, skv.SKV_BF16)
+    ws = torch.empty(skv.speckv_workspace_bytes(shape, cfg.C_max), dtype=torch.uint8, device=dev)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    scores = torch.empty((L, Hkv, cfg.n_pre), dtype=torch.float32, device=dev)
+    kept = torch.empty((L, Hkv, n_keep), dtype=torch.int32, device=dev)
+    kc = torch.empty((L, Hkv, n_keep, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], scores, ws)
+    skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, None, ws)
+    skv.speckv_compact(shape, inp["k_buf"], inp["v_buf"], kept, n_keep, kc, vc, ws)
+    g = torch.Generator(device=dev).manual_seed(args.seed or 7)
+    q = torch.randn((L, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def timed(sh, n_rows, k, v, reps):
+        n_ws = skv.speckv_decode_workspace_bytes(sh, n_rows)
+        w = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws else None
+        for _ in range(args.warmup):
+            skv.speckv_decode_attention(sh, n_rows, q, k, v, out, w, stream)
+        torch.cuda.synchronize()
+        skv.profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            skv.speckv_decode_attention(sh, n_rows, q, k, v, out, w, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prof = skv.profile_read()
+        skv.profile_enable(False)
+        n, t = prof["decode_attention"]
+        return e0.elapsed_time(e1) / reps, t / n
+
+    c_shape = skv.make_shape(L, Hq, Hkv, d, n_keep, 0, 0, skv.SKV_BF16)
+    reps_c = max(args.steps, 1) * 10
+    ms_c, kern_c = timed(c_shape, n_keep, kc, vc, reps_c)
+    ms_f, kern_f = timed(shape, cfg.n_in, inp["k_buf"], inp["v_buf"], max(args.steps, 1))
+    print(f"[bench] decode: compacted {ms_c * 1e3:.1f} us, full cache {ms_f * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    def alg_bytes(n_rows):  # K and V rows read once, the queries read, the fp32 outputs written
+        return L * Hkv * n_rows * d * 2 * 2 + L * Hq * d * 2 + L * Hq * d * 4
+
+    gbs_c = alg_bytes(n_keep) / (kern_c * 1e-3) / 1e9
+    gbs_f = alg_bytes(cfg.n_in) / (kern_f * 1e-3) / 1e9
+    return {
+        "metric": "decode attention over the compacted KV cache: layer-steps/sec (all layers, one token)",
+        "value": 1e3 / ms_c, "unit": "decode steps/s", "n_gpus": 1, "steps": reps_c, "warmup": args.warmup,
+        "ms_per_step": round(ms_c, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_" + cfg.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": d, "rows_compacted": n_keep, "rows_full": cfg.n_in},
+        "roofline": {"kernel": "decode_attention (full cache)", "bound": "hbm", "achieved": round(gbs_f, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs_f / PEAK_HBM_GBS, 4), "traffic": None},
+        "compacted": {"ms": round(ms_c, 5), "kernel_ms": round(kern_c, 5), "GBps": round(gbs_c, 1),
+                      "bytes": alg_bytes(n_keep)},
+        "full_cache": {"ms": round(ms_f, 4), "kernel_ms": round(kern_f, 4), "GBps": round(gbs_f, 1),
+                       "bytes": alg_bytes(cfg.n_in)},
+        "speedup_vs_full_cache": round(ms_f / ms_c, 1),
+    }, inp
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -334,6 +404,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "decode_qwen32b_shape_64k":
+        out, _ = bench_decode(args, wl.CONFIGS[3], torch, skv, wl)
+        print(json.dumps(out), flush=True)
+        return
     if args.workload in wl.CASCADES:
         out, _ = bench_cascade(args, wl.CASCADES[args.workload], torch, skv, wl)
         print(json.dumps(out), flush=True)

@@ -177,6 +177,31 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
                                const float* query_weights, float* token_scores, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Decode attention over a (compacted) KV cache ("Background": attention and
+ * KV cache cost grow with the context; "Key designs", SpecKV: generation
+ * runs over the kept pairs).  For every layer l and query head hq, with
+ * cache head h = hq / G (G = n_q_heads / n_kv_heads), or h = hq with
+ * per_query_head (one cache per query head, as speckv_compact writes it):
+ *   out[l][hq] = sum_{j < n_rows} softmax_j(scale * <q[l][hq], k[l][h][j]>) v[l][h][j]
+ * (no mask: every cached row precedes the new token; append the new
+ * token's own K/V row to attend it).
+ * The shape describes the cache buffers: k, v are [n_layers][H][kv_head_stride]
+ * with rows of head_dim elements, H = n_kv_heads (or n_q_heads with
+ * per_query_head), n_in rows allocated per head.  After out-of-place
+ * compaction pass n_in = n_rows = n_keep; after in-place compaction the
+ * prefill shape and n_rows = n_keep.  n_window, n_lookahead and aggregation
+ * are ignored.  bf16 only (SKV_ERR_DTYPE); G <= 16 (SKV_ERR_SHAPE).
+ * Inputs : q bf16 [n_layers][n_q_heads][head_dim]; k, v as above.
+ * Output : out float [n_layers][n_q_heads][head_dim].
+ * Requires 1 <= n_rows <= n_in (SKV_ERR_PARAM).  Long caches are split over
+ * several blocks per head, whose partial results go to the workspace;
+ * speckv_decode_workspace_bytes reports its size (0 bytes when every head
+ * fits one block, e.g. up to 512 rows; NULL is then allowed). */
+skv_status speckv_decode_workspace_bytes(const skv_shape* shape, int64_t n_rows, size_t* out_bytes);
+skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const void* q, const void* k,
+                                   const void* v, float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Optional per-kernel timing with HIP events, for measurement only.
  * While enabled, every kernel the library launches is bracketed by a pair
  * of events on its stream.  speckv_profile_read synchronizes on the

@@ -207,3 +207,25 @@ def test_gather_tokens_validation(lib):
     assert g(P((1 << 30) + 8), v, tok, 10, ko, vo) == ALIGN
     assert g(k, v, P((3 << 30) + 2), 10, ko, vo) == ALIGN
     assert lib.specpc_gather_tokens(None, k, v, tok, 10, ko, vo, None) == NULL
+
+
+def test_decode_validation(lib):
+    s = shape(n_in=288, n_window=16)  # a compacted cache of 288 rows per head (G = 4)
+    q, k, v, out, ws = P(1 << 30), P(2 << 30), P(3 << 30), P(4 << 30), P(5 << 30)
+    dec = lambda sh, n, *a: lib.speckv_decode_attention(ctypes.byref(sh), n, *a, None)
+    assert dec(s, 0, q, k, v, out, None, 0) == PARAM
+    assert dec(s, 289, q, k, v, out, None, 0) == PARAM
+    assert dec(s, 288, None, k, v, out, None, 0) == NULL
+    assert dec(shape(n_in=288, n_window=16, dtype=skv.SKV_F32), 288, q, k, v, out, None, 0) == DTYPE
+    assert dec(shape(n_in=288, n_window=16, n_q_heads=34, n_kv_heads=2), 288, q, k, v, out, None, 0) == SHAPE  # G 17
+    assert dec(s, 288, P((1 << 30) + 2), k, v, out, None, 0) == ALIGN
+    assert dec(s, 288, q, k, v, P((2 << 30) + 64), None, 0) == ALIAS  # output inside the K cache
+    # up to 512 rows: one block per head, no workspace; beyond: partials in the workspace
+    n = ctypes.c_size_t(7)
+    assert lib.speckv_decode_workspace_bytes(ctypes.byref(s), 288, ctypes.byref(n)) == OK and n.value == 0
+    long = shape(n_in=4096, n_window=16)
+    assert lib.speckv_decode_workspace_bytes(ctypes.byref(long), 4096, ctypes.byref(n)) == OK
+    assert n.value >= 2 * 2 * 8 * 16 * (8 + 128 * 4)  # layers x KV heads x chunks x 16 slots x (max, sum, acc)
+    assert dec(long, 4096, q, k, v, out, None, 0) == WS
+    assert dec(long, 4096, q, k, v, out, ws, n.value - 1) == WS
+    assert lib.speckv_decode_workspace_bytes(ctypes.byref(long), 0, ctypes.byref(n)) == PARAM
