@@ -117,3 +117,59 @@ def test_specpc_select_no_forced_window():
     s = np.linspace(1.0, 0.0, 40)
     kept, _ = oracle.specpc_select(s, 5, "max", 1)
     assert kept.tolist() == [0, 1, 2, 3, 4]
+
+
+# ---- n_lookahead > 1: draft rows at the end of the window, draft keys in their normaliser ----
+
+def test_lookahead_hand_example():
+    # n_in = 2 input tokens, n_lookahead = 2: one draft token at position 2; W = 2 rows at
+    # positions 1 and 2, d = 4, scale 1/2.  Row 0 (position 1, input) sees keys 0, 1 with
+    # logits (0, ln 3): (1/4, 3/4).  Row 1 (position 2, draft) sees keys 0, 1, 2 with logits
+    # (ln 2, 0, ln 5): (2/8, 1/8, 5/8); the input columns keep (1/4, 1/8).
+    # Weights (0.1, 1): scores = (max(0.025, 0.25), max(0.075, 0.125)) = (0.25, 0.125).
+    q = np.zeros((1, 1, 2, 4))
+    q[0, 0, 0, 0] = 1.0
+    q[0, 0, 1, 1] = 1.0
+    k = np.zeros((1, 1, 3, 4))
+    k[0, 0, 1, 0] = 2 * math.log(3)
+    k[0, 0, 0, 1] = 2 * math.log(2)
+    k[0, 0, 2, 1] = 2 * math.log(5)
+    abar = oracle.specpc_attention_mean(q, k, 0, n_in=2)
+    np.testing.assert_allclose(abar, [[0.25, 0.75], [0.25, 0.125]], rtol=1e-14)
+    np.testing.assert_allclose(oracle.specpc_token_scores(q, k, 0, n_in=2), [0.25, 0.125], rtol=1e-14)
+
+
+def test_lookahead_row_sums_and_reduction():
+    L, Hq, Hkv, W, d, n_in, n_la = 3, 4, 2, 6, 8, 30, 4
+    q = _rand((L, Hq, W, d), 31)
+    k = _rand((L, Hkv, n_in + n_la - 1, d), 32, 2.0)
+    abar = oracle.specpc_attention_mean(q, k, 1, n_in=n_in)
+    sums = abar.sum(axis=1)
+    # input rows (the first W - (n_la - 1)) see only input keys: they sum to one
+    np.testing.assert_allclose(sums[:W - (n_la - 1)], 1.0, atol=1e-14)
+    # draft rows lose exactly the mass their (causal) draft keys take
+    full = oracle.specpc_attention_mean(q, k, 1, n_in=n_in + n_la - 1)
+    np.testing.assert_allclose(sums + full[:, n_in:].sum(axis=1), 1.0, atol=1e-14)
+    assert (sums[W - (n_la - 1):] < 1.0).all()
+    # n_in = all keys is the n_lookahead = 1 form
+    np.testing.assert_array_equal(oracle.specpc_token_scores(q, k, 1, n_in=n_in + n_la - 1),
+                                  oracle.specpc_token_scores(q, k, 1))
+
+
+def test_lookahead_bruteforce_fsum():
+    W, d, n_in, n_la = 3, 3, 5, 3
+    q = _rand((1, 1, W, d), 33)
+    k = _rand((1, 1, n_in + n_la - 1, d), 34)
+    tau = 1 / math.sqrt(d)
+    n_keys = n_in + n_la - 1
+    w = oracle.default_query_weights(W)
+    want = [0.0] * n_in
+    for i in range(W):
+        pos = n_keys - W + i
+        logits = [tau * math.fsum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) for j in range(pos + 1)]
+        z = math.fsum(math.exp(x) for x in logits)
+        for j in range(n_in):
+            if j <= pos:
+                want[j] = max(want[j], w[i] * math.exp(logits[j]) / z)
+    got = oracle.specpc_token_scores(q, k, 0, n_in=n_in)
+    np.testing.assert_allclose(got, want, rtol=1e-13)
