@@ -86,10 +86,14 @@ struct PcWs {
   ScoreWs sc;
   size_t rowmax, end;
 };
+// SpecPC keys: the n_in input tokens, then the n_lookahead - 1 draft tokens
+// the window's draft rows attend (none when n_lookahead <= 1).
+int64_t specpc_keys(const Dims& d) { return d.n_in + (d.n_lookahead > 1 ? d.n_lookahead - 1 : 0); }
+
 PcWs specpc_ws(const Dims& d, int64_t units) {
   const int64_t G = d.Hq / d.Hkv, W = d.n_window;
   PcWs w;
-  w.sc = score_ws(d, units, G * W, d.n_in);
+  w.sc = score_ws(d, units, G * W, specpc_keys(d));
   const int64_t rpb = specpc_rows_per_block(d.dtype, (int)d.D);
   const int64_t nrb = (W + rpb - 1) / rpb;
   w.rowmax = w.sc.end;
@@ -464,6 +468,8 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
       (query_weights && !aligned(query_weights, 4)))
     return SKV_ERR_ALIGN;
   const int64_t G = d.Hq / d.Hkv, units = (d.L - l_skip) * d.Hkv;
+  const int64_t n_keys = specpc_keys(d);  // keys in the causal normaliser
+  if (d.stride < n_keys * d.D) return SKV_ERR_SHAPE;  // head slabs must hold the draft keys too
   const PcWs w = specpc_ws(d, units);
   if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
@@ -484,12 +490,12 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   a.group = (int32_t)G;
   a.rows_per_qhead = (int32_t)W;
   a.n_rows = (int32_t)(G * W);
-  a.n_keys = (int32_t)d.n_in;
+  a.n_keys = (int32_t)n_keys;
   ScorePlan pl;
-  score_plan(d.dtype, (int)d.D, units, G * W, d.n_in, &pl);
+  score_plan(d.dtype, (int)d.D, units, G * W, n_keys, &pl);
   apply_plan(a, pl);
   a.causal = 1;
-  a.pos_base = d.n_in - W;
+  a.pos_base = n_keys - W;  // window row i sits at position n_keys - W + i
   a.c = d.scale * 1.4426950408889634f;
   char* base = static_cast<char*>(ws);
   a.part = reinterpret_cast<float2*>(base + w.sc.part);
@@ -503,6 +509,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
   pa.n_rowblocks = (int32_t)((W + rpb - 1) / rpb);
   pa.inv_maps = (float)(1.0 / (double)(units * G));
   SKV_TRY(run_scoring(d, a, pl, s));
+  a.n_keys = (int32_t)d.n_in;  // the mean and max cover the input tokens only
   {
     ProfScope p("specpc_pass2", s);
     SKV_TRY(hip_status(launch_specpc_pass2(d.dtype, (int)d.D, pa, s)));

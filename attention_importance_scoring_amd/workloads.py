@@ -100,6 +100,11 @@ class SpecPCConfig:
         return self.n_q_heads // self.n_kv_heads
 
     @property
+    def n_keys(self) -> int:
+        """Positions of the draft's query and key axes: n_in + n_lookahead - 1 (n_in when n_lookahead <= 1)."""
+        return self.n_in + max(self.n_lookahead, 1) - 1
+
+    @property
     def torch_dtype(self):
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
@@ -224,14 +229,16 @@ def speckv_inputs(cfg: SpecKVConfig, seed: int, device="cpu", layers=None, kv_he
 
 
 def specpc_layer(cfg: SpecPCConfig, layer: int, seed: int, device="cpu"):
-    """One draft layer: q_win [Hq, W, d] (window queries), k [Hkv, n_in, d]."""
+    """One draft layer: q_win [Hq, W, d] (window queries), k [Hkv, n_keys, d]
+    (n_keys = n_in + n_lookahead - 1: the input tokens, then the draft tokens
+    the window's last rows are)."""
     d, Hq, Hkv, G, W = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.G, cfg.window
     q = _randn((Hq, W, d), _gen(seed, layer, "q", device), device)
-    k = _randn((Hkv, cfg.n_in, d), _gen(seed, layer, "k", device), device)
+    k = _randn((Hkv, cfg.n_keys, d), _gen(seed, layer, "k", device), device)
     gh = _gen(seed, layer, "hh", device)
     q_rounded = q.to(cfg.torch_dtype).float()
     u = _unit_mean_direction(q_rounded.reshape(Hkv, G * W, d))
-    n_pre = cfg.n_in - W  # planted keys lie before the window
+    n_pre = min(cfg.n_keys - W, cfg.n_in)  # planted keys are input tokens before the window
     n_hh = min(cfg.n_in // 100, max(n_pre - 1, 0))
     for h in range(Hkv):
         pos = torch.randperm(max(n_pre - 1, 0), generator=gh, device=device)[:n_hh] + 1
@@ -242,11 +249,11 @@ def specpc_layer(cfg: SpecPCConfig, layer: int, seed: int, device="cpu"):
 
 
 def specpc_inputs(cfg: SpecPCConfig, seed: int, device="cpu"):
-    """q_win [L, Hq, W, d] and k [L, Hkv, n_in, d] for all layers (skipped ones included)."""
+    """q_win [L, Hq, W, d] and k [L, Hkv, n_keys, d] for all layers (skipped ones included)."""
     L, d = cfg.n_layers, cfg.head_dim
     dt = cfg.torch_dtype
     q_win = torch.empty((L, cfg.n_q_heads, cfg.window, d), dtype=dt, device=device)
-    k = torch.empty((L, cfg.n_kv_heads, cfg.n_in, d), dtype=dt, device=device)
+    k = torch.empty((L, cfg.n_kv_heads, cfg.n_keys, d), dtype=dt, device=device)
     for layer in range(L):
         q_win[layer], k[layer] = specpc_layer(cfg, layer, seed, device)
     return {"q_win": q_win, "k": k}

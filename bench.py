@@ -41,6 +41,8 @@ def parse():
                    help="SpecKV: aggregate the observation rows' probabilities by sum (default) or max")
     p.add_argument("--per-query-head", action="store_true",
                    help="SpecKV: one kept set (and compacted cache) per query head instead of per KV head")
+    p.add_argument("--n-lookahead", type=int, default=None,
+                   help="SpecPC: draft lookahead tokens (default: the workload's; > 1 puts draft rows in the window)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
     p.add_argument("--seed", type=int, default=0)
@@ -202,10 +204,12 @@ def bench_speckv(args, cfg, torch, skv, wl):
 
 def bench_specpc(args, cfg, torch, skv, wl):
     dev = "cuda"
+    if args.n_lookahead is not None:
+        cfg = wl.reduced(cfg, n_lookahead=args.n_lookahead)
     inp = wl.specpc_inputs(cfg, seed=args.seed or 5, device=dev)
     dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
     shape = skv.make_shape(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_in, cfg.window,
-                           cfg.n_lookahead, dt)
+                           cfg.n_lookahead, dt, kv_head_stride=cfg.n_keys * cfg.head_dim)
     sel = skv.make_shape(1, 1, 1, cfg.head_dim, cfg.n_in, 0, 0, dt)
     ws = torch.empty(skv.speckv_workspace_bytes(shape, 0), dtype=torch.uint8, device=dev)
     ts = torch.empty(cfg.n_in, dtype=torch.float32, device=dev)
@@ -233,7 +237,7 @@ def bench_specpc(args, cfg, torch, skv, wl):
     kern = {name: {"avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
             for name, (n, t) in prof.items()}
     maps = (cfg.n_layers - cfg.l_skip) * cfg.n_q_heads
-    elems = maps * sum(min(cfg.n_in, cfg.n_in - cfg.window + i + 1) for i in range(cfg.window))
+    elems = maps * sum(min(cfg.n_keys, cfg.n_keys - cfg.window + i + 1) for i in range(cfg.window))
     exps_per_s = 2 * elems / (ms * 1e-3)  # two passes, one exp per (row, visible key) each
     return {
         "metric": "SpecPC tokens scored+selected/sec (draft attention stack)", "value": cfg.n_in / (ms * 1e-3),
@@ -241,7 +245,7 @@ def bench_specpc(args, cfg, torch, skv, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "l_skip": cfg.l_skip, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "n_in": cfg.n_in, "window": cfg.window,
-                   "k_top": cfg.k_top},
+                   "n_lookahead": cfg.n_lookahead, "k_top": cfg.k_top},
         "exp_rate_per_s": exps_per_s, "kernels": kern,
     }, inp
 

@@ -162,15 +162,20 @@ skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const voi
                                 int64_t n_tokens, void* k_out, void* v_out, void* stream);
 
 /* SpecPC token scores ("Key designs", SpecPC).
- * For layers l_skip <= l < n_layers and every query head hq, window row i
- * (position p_i = n_in - W + i, W = n_window) attends causally:
+ * The draft's query axis has n_keys = n_in + n_lookahead - 1 positions (the
+ * input tokens, then the generated draft tokens but the last; n_keys = n_in
+ * when n_lookahead <= 1), and so does its key axis.  For layers
+ * l_skip <= l < n_layers and every query head hq, window row i (position
+ * p_i = n_keys - W + i, W = n_window) attends causally:
  *   P[l][hq][i][j] = softmax over j <= p_i of scale * <q_i, k_j>, 0 for j > p_i
- *   Abar[i][j]     = mean over (l, hq) of P
+ *   Abar[i][j]     = mean over (l, hq) of P, for the input tokens j < n_in
  *   token_scores[j] = max over i of w_i * Abar[i][j]
  * query_weights: float [W] on the device, or NULL for w_i = 0.1 + 0.9 i/(W-1)
  * (1 at the end of the window, 0.1 at its far edge; 1 when W = 1).
  * Inputs : q_win [n_layers][n_q_heads][W][head_dim] (all layers, skipped
- *          ones included), k.  Output: token_scores float [n_in].
+ *          ones included), k [n_layers][n_kv_heads][kv_head_stride] with
+ *          n_keys rows per head (kv_head_stride >= n_keys * head_dim,
+ *          SKV_ERR_SHAPE otherwise).  Output: token_scores float [n_in].
  * Requires 0 <= l_skip < n_layers, 1 <= W <= n_in, G * W <= 2^20, and
  * aggregation = per_query_head = 0 (SKV_ERR_PARAM otherwise). */
 skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,

@@ -154,6 +154,13 @@ def test_specpc_validation(lib):
         ctypes.byref(s), l_skip, P(1 << 20), P(1 << 24), None, P(1 << 26), ws, nb, None)
     assert f(-1) == PARAM and f(2) == PARAM
     assert f(1, None) == WS and f(1, P(1 << 28), 10) == WS
+    # with n_lookahead > 1 the head slabs must also hold the n_lookahead - 1 draft keys
+    sl = shape(n_window=512, n_lookahead=8, n_in=4096)
+    assert lib.specpc_token_scores(ctypes.byref(sl), 1, P(1 << 20), P(1 << 24), None, P(1 << 26), P(1 << 28),
+                                   1 << 30, None) == SHAPE
+    sl = shape(n_window=512, n_lookahead=8, n_in=4096, kv_head_stride=4103 * 128)
+    assert lib.specpc_token_scores(ctypes.byref(sl), 1, P(1 << 20), P(1 << 24), None, P(1 << 26), P(1 << 28),
+                                   10, None) == WS
     s0 = shape(n_window=0)
     assert lib.specpc_token_scores(ctypes.byref(s0), 0, P(1 << 20), P(1 << 24), None, P(1 << 26), P(1 << 28),
                                    1 << 30, None) == SHAPE

@@ -224,11 +224,12 @@ def test_config2_llama_shape_two_layers_full_length():
 
 def _specpc_check(cfg, seed, weights=None):
     print(f"\n[case] specpc L={cfg.n_layers} l_skip={cfg.l_skip} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} "
-          f"d={cfg.head_dim} {cfg.dtype} n_in={cfg.n_in} W={cfg.window} seed={seed}", flush=True)
+          f"d={cfg.head_dim} {cfg.dtype} n_in={cfg.n_in} W={cfg.window} lookahead={cfg.n_lookahead} seed={seed}",
+          flush=True)
     host = wl.specpc_inputs(cfg, seed, "cpu")
     dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
     shape = skv.make_shape(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_in, cfg.window,
-                           cfg.n_lookahead, dt)
+                           cfg.n_lookahead, dt, kv_head_stride=cfg.n_keys * cfg.head_dim)
     ws = workspace(shape, 0)
     q, k = host["q_win"].cuda(), host["k"].cuda()
     ts = torch.full((cfg.n_in,), float("nan"), dtype=torch.float32, device="cuda")
@@ -240,7 +241,8 @@ def _specpc_check(cfg, seed, weights=None):
     skv.speckv_select(sel_shape, ts, cfg.k_top, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws)
     torch.cuda.synchronize()
     want = oracle.specpc_token_scores(np64(host["q_win"]), np64(host["k"]), cfg.l_skip,
-                                      None if weights is None else np.asarray(weights, dtype=np.float64))
+                                      None if weights is None else np.asarray(weights, dtype=np.float64),
+                                      n_in=cfg.n_in)
     assert_scores_close(ts.cpu().numpy(), want, cfg.G, cfg.window, "token scores")
     pooled_o = oracle.pool1d(want, cfg.pool_kernel, "max")
     assert_kept_matches(kept.cpu().numpy()[None], pooled.cpu().numpy()[None], pooled_o[None], cfg.k_top, 0,
@@ -252,7 +254,11 @@ def _specpc_check(cfg, seed, weights=None):
     dict(n_layers=2, l_skip=0, n_in=777, window=1, k_top=700),
     dict(n_layers=2, l_skip=1, n_in=300, window=300, k_top=30),
     dict(n_layers=2, l_skip=0, n_in=900, window=77, k_top=64, head_dim=128),
-], ids=["ragged", "single-window-row", "window-equals-input", "d128-group-over-two-stages"])
+    dict(n_layers=3, l_skip=1, n_in=1000, window=100, k_top=64, n_lookahead=8),
+    dict(n_layers=2, l_skip=0, n_in=500, window=40, k_top=64, n_lookahead=40),
+    dict(n_layers=2, l_skip=1, n_in=700, window=90, k_top=64, n_lookahead=300, head_dim=128),
+], ids=["ragged", "single-window-row", "window-equals-input", "d128-group-over-two-stages", "lookahead-8",
+        "window-of-draft-rows", "lookahead-past-window-d128"])
 def test_specpc_small(case):
     _specpc_check(wl.reduced(wl.CONFIGS[5], **case), seed=21)
 
@@ -266,3 +272,8 @@ def test_specpc_user_weights_and_fp32():
 def test_specpc_config5_two_used_layers_full_length():
     # full n_in and W of the draft workload with 2 of the 20 used layers
     _specpc_check(wl.reduced(wl.CONFIGS[5], n_layers=6), seed=5)
+
+
+def test_specpc_config5_lookahead_16_two_used_layers():
+    # the draft workload with 16 lookahead tokens: 15 draft rows end the window
+    _specpc_check(wl.reduced(wl.CONFIGS[5], n_layers=6, n_lookahead=16), seed=6)
