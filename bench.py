@@ -42,7 +42,10 @@ def parse():
     p.add_argument("--per-query-head", action="store_true",
                    help="SpecKV: one kept set (and compacted cache) per query head instead of per KV head")
     p.add_argument("--n-lookahead", type=int, default=None,
-                   help="SpecPC: draft lookahead tokens (default: the workload's; > 1 puts draft rows in the window)")
+                   help="draft lookahead tokens (default: the workload's).  SpecKV: 0 scores with the window "
+                        "queries only; SpecPC: > 1 puts draft rows at the end of the window")
+    p.add_argument("--pool-kernel", type=int, default=None,
+                   help="SpecKV: max-pool width before selection (odd; 1 = no pooling; default: the workload's)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
     p.add_argument("--seed", type=int, default=0)
@@ -116,6 +119,10 @@ def traffic_for(kernel: str, workload: str):
 def bench_speckv(args, cfg, torch, skv, wl):
     from_layers = None
     dev = "cuda"
+    if args.n_lookahead is not None:
+        cfg = wl.reduced(cfg, n_lookahead=args.n_lookahead)
+    if args.pool_kernel is not None:
+        cfg = wl.reduced(cfg, pool_kernel=args.pool_kernel)
     t0 = time.perf_counter()
     inp = wl.speckv_inputs(cfg, seed=args.seed or 3, device=dev, layers=from_layers)
     torch.cuda.synchronize()
@@ -173,7 +180,8 @@ def bench_speckv(args, cfg, torch, skv, wl):
 
     keys = cfg.keys_per_call  # KV pairs scored and compacted (each query head's copy counted once)
     flops_per_pass = 2.0 * cfg.n_obs * cfg.n_q_heads * L * cfg.n_pre * d  # one Q_obs K^T over every head
-    default_variant = args.aggregation == "sum" and not args.per_query_head
+    default_variant = (args.aggregation == "sum" and not args.per_query_head and args.n_lookahead is None
+                       and args.pool_kernel is None)
     kern = {name: {"launches": n, "avg_ms": t / max(n, 1), "ms_per_step": t / args.steps} for name, (n, t) in prof.items()}
     # dominant kernel: the longer of the two scoring passes (each computes one Q_obs K^T)
     dom = max(("score_pass1", "score_pass2"), key=lambda k: kern[k]["ms_per_step"])
