@@ -33,7 +33,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["attention_importance_scoring_amd/csrc/" + f for f in
-                  ("common.hpp", "kernels.hpp", "score.hip", "select.hip", "specpc.hip", "capi.hip")]
+                  ("common.hpp", "kernels.hpp", "score.hip", "select.hip", "specpc.hip", "decode.hip", "capi.hip")]
 CALIB_PATTERN = "neg_kernel"
 
 
@@ -46,7 +46,9 @@ def kernel_source_hash() -> str:
 
 
 def short_name(kernel_name: str) -> str:
-    """'void skv::score_pass1_kernel<skv::bf16_t, 128>(skv::ScoreArgs)' -> 'score_pass1_kernel<bf16_t, 128>'."""
+    """'void skv::score_pass1_kernel<skv::bf16_t, 128>(skv::ScoreArgs)' -> 'score_pass1_kernel<bf16_t, 128>'
+    (kernels in an anonymous namespace inside skv included)."""
+    kernel_name = kernel_name.replace("(anonymous namespace)::", "")
     m = re.search(r"skv::(\w+)(<[^()]*>)?", kernel_name)
     if m:
         return m.group(1) + (m.group(2) or "").replace("skv::", "")
@@ -102,7 +104,7 @@ def traffic(fetch_dir: str, write_dir: str, calib_mib: int) -> dict:
     f_scale, w_scale = known_kib / f_cal, known_kib / w_cal
     kernels = {}
     for name in sorted(set(fetch) & set(write)):
-        if not name.startswith(("score_", "lse_", "select", "gather", "specpc_")):
+        if not name.startswith(("score_", "lse_", "select", "gather", "specpc_", "decode_", "colsum_")):
             continue
         f = sum(fetch[name]) / len(fetch[name])
         w = sum(write[name]) / len(write[name])

@@ -25,7 +25,7 @@ METRIC = "keys scored+compacted/sec and % of HBM/MFMA roofline at n_in=64K, 32B 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "speckv_kernels_{workload}_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -46,6 +46,8 @@ def parse():
                         "queries only; SpecPC: > 1 puts draft rows at the end of the window")
     p.add_argument("--pool-kernel", type=int, default=None,
                    help="SpecKV: max-pool width before selection (odd; 1 = no pooling; default: the workload's)")
+    p.add_argument("--decode-cache", choices=["both", "compacted", "full"], default="both",
+                   help="decode workload: time decode over the compacted cache, the full cache, or both")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
     p.add_argument("--seed", type=int, default=0)
@@ -98,13 +100,44 @@ def speckv_cpu_baseline(cfg, inp, budget_s=12.0):
                       f"{t_total:.1f} s of fp64 NumPy"}
 
 
-def traffic_for(kernel: str, workload: str):
+def decode_cpu_baseline(cfg, inp, cache, budget_s=10.0):
+    """The fp64 decode-attention oracle on whole (layer, KV head) units of
+    the same caches (the compacted 288-row one unless only the full cache is
+    benchmarked), until ~budget_s of work; scaled to all-layer decode steps/s."""
+    import numpy as np
+    import oracle
+    from attention_importance_scoring_amd import workloads as wl
+    G, d = cfg.G, cfg.head_dim
+    L, H = cfg.n_layers, cfg.n_kv_heads
+    n_rows = cfg.n_keep if cache != "full" else cfg.n_in
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, G, d))
+    done, t_total = 0, 0.0
+    for idx in rng.permutation(L * H):
+        layer, h = divmod(int(idx), H)
+        k = wl.to_numpy_f64(inp["k"][layer:layer + 1, h:h + 1, :n_rows])
+        v = wl.to_numpy_f64(inp["v"][layer:layer + 1, h:h + 1, :n_rows])
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, k, v)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    per_step = t_total / done * (L * H)
+    return {"value": 1.0 / per_step, "unit": "decode steps/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{done} of {L * H} (layer, KV head) units, {n_rows} rows each (the first rows of the "
+                      f"full cache stand in for the compacted ones), {t_total:.2f} s of fp64 NumPy, scaled to "
+                      f"all {L * H} units"}
+
+
+def traffic_for(kernel: str, workload: str, summary: str):
     """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)
-    from the committed counter summary, or None when it is absent, covers
-    another workload or was taken on different kernel sources."""
+    from the committed counter summary profiles/<summary>, or None when it
+    is absent, covers another workload or was taken on different kernel
+    sources."""
     from attention_importance_scoring_amd.counters import kernel_source_hash
     try:
-        with open(TRAFFIC_FILE.format(workload=workload)) as f:
+        with open(os.path.join(PROFILES, summary)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -191,7 +224,7 @@ def bench_speckv(args, cfg, torch, skv, wl):
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = flops_per_launch / avg_s / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name) if default_variant else None}
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name, f"speckv_kernels_{cfg.name}_traffic.json") if default_variant else None}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
     path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
     out = {
@@ -374,32 +407,43 @@ def bench_decode(args, cfg, torch, skv, wl):
         n, t = prof["decode_attention"]
         return e0.elapsed_time(e1) / reps, t / n
 
-    c_shape = skv.make_shape(L, Hq, Hkv, d, n_keep, 0, 0, skv.SKV_BF16)
-    reps_c = max(args.steps, 1) * 10
-    ms_c, kern_c = timed(c_shape, n_keep, kc, vc, reps_c)
-    ms_f, kern_f = timed(shape, cfg.n_in, inp["k_buf"], inp["v_buf"], max(args.steps, 1))
-    print(f"[bench] decode: compacted {ms_c * 1e3:.1f} us, full cache {ms_f * 1e3:.1f} us", file=sys.stderr, flush=True)
-
     def alg_bytes(n_rows):  # K and V rows read once, the queries read, the fp32 outputs written
         return L * Hkv * n_rows * d * 2 * 2 + L * Hq * d * 2 + L * Hq * d * 4
 
-    gbs_c = alg_bytes(n_keep) / (kern_c * 1e-3) / 1e9
-    gbs_f = alg_bytes(cfg.n_in) / (kern_f * 1e-3) / 1e9
-    return {
-        "metric": "decode attention over the compacted KV cache: layer-steps/sec (all layers, one token)",
-        "value": 1e3 / ms_c, "unit": "decode steps/s", "n_gpus": 1, "steps": reps_c, "warmup": args.warmup,
-        "ms_per_step": round(ms_c, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+    res = {}
+    if args.decode_cache in ("both", "compacted"):
+        c_shape = skv.make_shape(L, Hq, Hkv, d, n_keep, 0, 0, skv.SKV_BF16)
+        reps = max(args.steps, 1) * 10
+        ms, kern = timed(c_shape, n_keep, kc, vc, reps)
+        res["compacted"] = {"ms": round(ms, 5), "kernel_ms": round(kern, 5), "reps": reps, "rows": n_keep,
+                            "GBps": round(alg_bytes(n_keep) / (kern * 1e-3) / 1e9, 1), "bytes": alg_bytes(n_keep)}
+    if args.decode_cache in ("both", "full"):
+        reps = max(args.steps, 1)
+        ms, kern = timed(shape, cfg.n_in, inp["k_buf"], inp["v_buf"], reps)
+        res["full_cache"] = {"ms": round(ms, 4), "kernel_ms": round(kern, 4), "reps": reps, "rows": cfg.n_in,
+                             "GBps": round(alg_bytes(cfg.n_in) / (kern * 1e-3) / 1e9, 1),
+                             "bytes": alg_bytes(cfg.n_in)}
+    print(f"[bench] decode: {json.dumps(res)}", file=sys.stderr, flush=True)
+    head = res.get("compacted") or res["full_cache"]
+    out = {
+        "metric": "decode attention over the " + ("compacted" if "compacted" in res else "full") +
+                  " KV cache: layer-steps/sec (all layers, one token)",
+        "value": 1e3 / head["ms"], "unit": "decode steps/s", "n_gpus": 1, "steps": head["reps"],
+        "warmup": args.warmup, "ms_per_step": head["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode_" + cfg.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "head_dim": d, "rows_compacted": n_keep, "rows_full": cfg.n_in},
-        "roofline": {"kernel": "decode_attention (full cache)", "bound": "hbm", "achieved": round(gbs_f, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs_f / PEAK_HBM_GBS, 4), "traffic": None},
-        "compacted": {"ms": round(ms_c, 5), "kernel_ms": round(kern_c, 5), "GBps": round(gbs_c, 1),
-                      "bytes": alg_bytes(n_keep)},
-        "full_cache": {"ms": round(ms_f, 4), "kernel_ms": round(kern_f, 4), "GBps": round(gbs_f, 1),
-                       "bytes": alg_bytes(cfg.n_in)},
-        "speedup_vs_full_cache": round(ms_f / ms_c, 1),
-    }, inp
+                   "head_dim": d, "rows_compacted": n_keep, "rows_full": cfg.n_in, "cache": args.decode_cache},
+    }
+    if "full_cache" in res:
+        f = res["full_cache"]
+        out["roofline"] = {"kernel": "decode_attention (full cache)", "bound": "hbm", "achieved": f["GBps"],
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(f["GBps"] / PEAK_HBM_GBS, 4),
+                           "traffic": traffic_for("decode_attention", "decode_" + cfg.name,
+                                                  f"decode_attention_{cfg.name}_traffic.json")}
+    out.update(res)
+    if len(res) == 2:
+        out["speedup_vs_full_cache"] = round(res["full_cache"]["ms"] / res["compacted"]["ms"], 1)
+    return out, inp
 
 
 def main():
@@ -416,16 +460,13 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    cfg = {c.name: c for c in wl.CONFIGS.values()}.get(args.workload)
     if args.workload == "decode_qwen32b_shape_64k":
-        out, _ = bench_decode(args, wl.CONFIGS[3], torch, skv, wl)
-        print(json.dumps(out), flush=True)
-        return
-    if args.workload in wl.CASCADES:
-        out, _ = bench_cascade(args, wl.CASCADES[args.workload], torch, skv, wl)
-        print(json.dumps(out), flush=True)
-        return
-    cfg = {c.name: c for c in wl.CONFIGS.values()}[args.workload]
-    if args.workload == "specpc_draft_32k":
+        cfg = wl.CONFIGS[3]
+        out, inp = bench_decode(args, cfg, torch, skv, wl)
+    elif args.workload in wl.CASCADES:
+        out, inp = bench_cascade(args, wl.CASCADES[args.workload], torch, skv, wl)
+    elif args.workload == "specpc_draft_32k":
         out, inp = bench_specpc(args, cfg, torch, skv, wl)
     else:
         out, inp = bench_speckv(args, cfg, torch, skv, wl)
@@ -438,7 +479,11 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n * 4
-    if not args.no_cpu_baseline and args.workload != "specpc_draft_32k":
+    if not args.no_cpu_baseline and args.workload == "decode_qwen32b_shape_64k":
+        print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = decode_cpu_baseline(cfg, inp, args.decode_cache)
+    elif not args.no_cpu_baseline and args.workload in {c.name for c in wl.CONFIGS.values()} \
+            and args.workload != "specpc_draft_32k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = speckv_cpu_baseline(cfg, inp)
     print(json.dumps(out), flush=True)
