@@ -521,7 +521,7 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
 size_t decode_ws_bytes(const Dims& d, int64_t n_rows) {
   const int64_t units = d.L * d.heads();
   int32_t n_sub = 1, chunks = 1;
-  decode_plan(units, n_rows, &n_sub, &chunks);
+  decode_plan(d.dtype, units, n_rows, &n_sub, &chunks);
   if (chunks <= 1) return 0;
   const int64_t slots = units * chunks * decode_max_group();
   return round_up((size_t)slots * sizeof(float2)) + round_up((size_t)(slots * d.D) * sizeof(float));
@@ -540,7 +540,6 @@ skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const
                                    const void* v, float* out, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   SKV_TRY(check_shape(shape, &d));
-  if (d.dtype != SKV_BF16) return SKV_ERR_DTYPE;
   if (!q || !k || !v || !out) return SKV_ERR_NULL;
   if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
   if (d.group() > decode_max_group()) return SKV_ERR_SHAPE;
@@ -562,7 +561,7 @@ skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const
   a.heads_per_layer = (int32_t)d.heads();
   a.q_heads_per_layer = (int32_t)d.Hq;
   a.group = (int32_t)d.group();
-  decode_plan(units, n_rows, &a.n_sub, &a.n_chunks);
+  decode_plan(d.dtype, units, n_rows, &a.n_sub, &a.n_chunks);
   a.c = d.scale * 1.4426950408889634f;
   a.out = out;
   if (need > 0) {
@@ -577,7 +576,7 @@ skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   ProfScope p("decode_attention", s);
-  return hip_status(launch_decode_attention((int)d.D, a, s));
+  return hip_status(launch_decode_attention(d.dtype, (int)d.D, a, s));
 }
 
 skv_status speckv_profile_enable(int32_t on) {

@@ -22,9 +22,11 @@
 //
 // P enters the MFMA as two bf16 terms, p = hi + lo (hi = bf16(p),
 // lo = bf16(p - hi)), so the product carries about 16 bits of P; the second
-// MFMA is free in an HBM-bound kernel.
+// MFMA is free in an HBM-bound kernel.  fp32 caches use
+// v_mfma_f32_16x16x4f32 with the same lane layout (one contraction element
+// per lane and step), exact fp32 P and two tiles per wave per sub-chunk.
 //
-// A block walks n_sub sub-chunks of 512 keys (128 per wave).  In each, a
+// A block walks n_sub sub-chunks of 512 keys (256 for fp32).  In each, a
 // wave first computes all scores of its four tiles (kept in registers) and
 // their exact maximum, then the probabilities and P V; its running (max,
 // sum, acc) is rescaled once per sub-chunk, only when the maximum grows.
@@ -43,19 +45,24 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kDecTilesPerWave = 4;                          // 32-key tiles per wave per sub-chunk
-constexpr int kDecSub = kDecWaves * kDecTilesPerWave * 32;    // keys per sub-chunk
-constexpr int kDecMaxGroup = 16;                             // queries per cache head (MFMA N)
+constexpr int kDecMaxGroup = 16;  // queries per cache head (MFMA N)
 
-template <int D>
+template <typename T, int D>
 struct DecGeom {
-  static constexpr int kSteps = D / 32;          // QK MFMAs per 16-key half tile
-  static constexpr int kDGroups = D / 16;        // PV MFMAs (16 head-dim columns each) per term
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kPitch = kRowBytes + 8;   // LDS V row pitch: the 4 key groups of a read hit distinct banks
+  static constexpr bool kF32 = Elem<T>::kBytes == 4;
+  static constexpr int kTiles = kF32 ? 2 : 4;                // 32-key tiles per wave per sub-chunk
+  static constexpr int kSubKeys = kDecWaves * kTiles * 32;   // keys per sub-chunk
+  static constexpr int kRowBytes = D * Elem<T>::kBytes;
+  // Q and K operand: in vector s, lane (row r, group g) holds bytes
+  // [64 s + 16 g, 64 s + 16 g + 16) of its row, so the four lanes of a row
+  // read 64 contiguous bytes per vector.
+  static constexpr int kQV = kRowBytes / 64;
+  static constexpr int kDGroups = D / 16;                    // PV MFMAs (16 head-dim columns each) per term
+  // LDS V row pitch: the four key groups of one transposed read hit distinct banks
+  static constexpr int kPitch = kRowBytes + (kF32 ? 16 : 8);
   static constexpr int kVecPerRow = kRowBytes / 16;
-  static constexpr int kVLoads = 32 * kVecPerRow / kWave;  // 16-byte V loads per lane per tile
-  static constexpr int kWaveLds = 32 * kPitch;             // V tile bytes per wave
+  static constexpr int kVLoads = 32 * kVecPerRow / kWave;    // 16-byte V loads per lane per tile
+  static constexpr int kWaveLds = 32 * kPitch;               // V tile bytes per wave
   static constexpr int kMergeLds = kDecWaves * (kDecMaxGroup * D + 2 * kDecMaxGroup) * 4;
   static constexpr int kLds = kDecWaves * kWaveLds > kMergeLds ? kDecWaves * kWaveLds : kMergeLds;
 };
@@ -64,14 +71,29 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8 a, bf16x8 b, f32x4_t acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// acc += A B over one 16-byte vector of each operand: one bf16 MFMA (8
+// contraction elements per lane), or four fp32 MFMAs (one element each).
+template <typename T>
+__device__ __forceinline__ f32x4_t mfma_vec(u32x4 a, u32x4 b, f32x4_t acc) {
+  if constexpr (Elem<T>::kBytes == 2) {
+    return mfma16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
 __device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16); }
 
-// Key (within a 32-key tile) of A/B element e for key group g = lane / 16.
+// Key (within a 32-key tile) of P/V contraction element e for key group g = lane / 16.
 __device__ __forceinline__ int tile_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(DecodeArgs a) {
-  using Geo = DecGeom<D>;
+  using Geo = DecGeom<T, D>;
+  constexpr int TW = Geo::kTiles;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -80,17 +102,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(Decode
   const int G = a.group;
   const int64_t layer = unit / a.heads_per_layer, head = unit % a.heads_per_layer;
   const int64_t q_row0 = layer * a.q_heads_per_layer + head * G;  // first query (and output) row of the unit
-  const char* kp = static_cast<const char*>(a.k) + unit * a.head_stride * 2;
-  const char* vp = static_cast<const char*>(a.v) + unit * a.head_stride * 2;
+  const char* kp = static_cast<const char*>(a.k) + unit * a.head_stride * Elem<T>::kBytes;
+  const char* vp = static_cast<const char*>(a.v) + unit * a.head_stride * Elem<T>::kBytes;
 
-  // Q^T operand: in MFMA step s, lane (query r, group g) holds head-dim
-  // elements [32 s + 8 g, 32 s + 8 g + 8), so the four lanes of a row read
-  // 64 contiguous bytes per step; padded queries are zero.
-  u32x4 qf[Geo::kSteps];
+  // Q^T operand (queries on N); padded queries are zero.
+  u32x4 qf[Geo::kQV];
   {
     const char* qp = static_cast<const char*>(a.q) + (q_row0 + (r < G ? r : 0)) * Geo::kRowBytes + 16 * g;
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) {
+    for (int s = 0; s < Geo::kQV; ++s) {
       qf[s] = ldg16(qp + 64 * s);
       if (r >= G) qf[s] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -104,34 +124,34 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(Decode
   float m = -INFINITY;     // running maximum for query r (log2 units), the same in the four lanes of r
 
   for (int sub = 0; sub < a.n_sub; ++sub) {
-    const int64_t sub_base = ((int64_t)chunk * a.n_sub + sub) * kDecSub;
+    const int64_t sub_base = ((int64_t)chunk * a.n_sub + sub) * Geo::kSubKeys;
     if (sub_base > last) break;  // block-uniform
 
     // ---- phase 1: scores of this wave's tiles (tile t = wave + 4 j of the sub-chunk) ----
     // Every load is issued before the first MFMA; rows past the cache end are
     // clamped to its last row (in bounds) and masked below.
-    u32x4 kf[kDecTilesPerWave][2][Geo::kSteps];
+    u32x4 kf[TW][2][Geo::kQV];
 #pragma unroll
-    for (int j = 0; j < kDecTilesPerWave; ++j) {
+    for (int j = 0; j < TW; ++j) {
       const int64_t kbase = sub_base + 32 * (wave + kDecWaves * j);
       const int64_t ra = kbase + r < last ? kbase + r : last;
       const int64_t rb = kbase + 16 + r < last ? kbase + 16 + r : last;
 #pragma unroll
-      for (int s = 0; s < Geo::kSteps; ++s) {
+      for (int s = 0; s < Geo::kQV; ++s) {
         kf[j][0][s] = ldg16(kp + ra * Geo::kRowBytes + 16 * g + 64 * s);
         kf[j][1][s] = ldg16(kp + rb * Geo::kRowBytes + 16 * g + 64 * s);
       }
     }
-    float sc[kDecTilesPerWave][8];
+    float sc[TW][8];
     float m_sub = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kDecTilesPerWave; ++j) {
+    for (int j = 0; j < TW; ++j) {
       const int64_t kbase = sub_base + 32 * (wave + kDecWaves * j);
       f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < Geo::kSteps; ++s) {
-        sa = mfma16(__builtin_bit_cast(bf16x8, kf[j][0][s]), __builtin_bit_cast(bf16x8, qf[s]), sa);
-        sb = mfma16(__builtin_bit_cast(bf16x8, kf[j][1][s]), __builtin_bit_cast(bf16x8, qf[s]), sb);
+      for (int s = 0; s < Geo::kQV; ++s) {
+        sa = mfma_vec<T>(kf[j][0][s], qf[s], sa);
+        sb = mfma_vec<T>(kf[j][1][s], qf[s], sb);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -162,9 +182,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(Decode
     // All V tiles of the wave are requested at once (16-byte vectors,
     // consecutive lanes along a row: fully used lines), then staged through
     // LDS one tile at a time for the transposed reads.
-    u32x4 vv[kDecTilesPerWave][Geo::kVLoads];
+    u32x4 vv[TW][Geo::kVLoads];
 #pragma unroll
-    for (int j = 0; j < kDecTilesPerWave; ++j) {
+    for (int j = 0; j < TW; ++j) {
       const int64_t kbase = sub_base + 32 * (wave + kDecWaves * j);
 #pragma unroll
       for (int t = 0; t < Geo::kVLoads; ++t) {
@@ -175,17 +195,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(Decode
       }
     }
 #pragma unroll
-    for (int j = 0; j < kDecTilesPerWave; ++j) {
+    for (int j = 0; j < TW; ++j) {
       const int64_t kbase = sub_base + 32 * (wave + kDecWaves * j);
       if (kbase > last) continue;  // wave-uniform: a tile past the end holds no key
-      bf16x8 phi, plo;
+      float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(sc[j][e] - m);  // 0 for masked keys
-        l += p;
-        const __bf16 h = (__bf16)p;
-        phi[e] = h;
-        plo[e] = (__bf16)(p - (float)h);
+        p[e] = fast_exp2(sc[j][e] - m);  // 0 for masked keys
+        l += p[e];
       }
 #pragma unroll
       for (int t = 0; t < Geo::kVLoads; ++t) {
@@ -197,14 +214,31 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_attention_kernel(Decode
       }
       // LDS operations of one wave complete in issue order: the reads below see the writes above
       __builtin_amdgcn_wave_barrier();
-      const __bf16* vt = reinterpret_cast<const __bf16*>(vl);
+      if constexpr (Geo::kF32) {
+        const float* vt = reinterpret_cast<const float*>(vl);
 #pragma unroll
-      for (int dg = 0; dg < Geo::kDGroups; ++dg) {
-        bf16x8 vb;
+        for (int dg = 0; dg < Geo::kDGroups; ++dg)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vb[e] = vt[tile_key(g, e) * (Geo::kPitch / 2) + 16 * dg + r];
-        acc[dg] = mfma16(phi, vb, acc[dg]);
-        acc[dg] = mfma16(plo, vb, acc[dg]);
+          for (int e = 0; e < 8; ++e)
+            acc[dg] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                p[e], vt[tile_key(g, e) * (Geo::kPitch / 4) + 16 * dg + r], acc[dg], 0, 0, 0);
+      } else {
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 h = (__bf16)p[e];
+          phi[e] = h;
+          plo[e] = (__bf16)(p[e] - (float)h);
+        }
+        const __bf16* vt = reinterpret_cast<const __bf16*>(vl);
+#pragma unroll
+        for (int dg = 0; dg < Geo::kDGroups; ++dg) {
+          bf16x8 vb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vb[e] = vt[tile_key(g, e) * (Geo::kPitch / 2) + 16 * dg + r];
+          acc[dg] = mfma16(phi, vb, acc[dg]);
+          acc[dg] = mfma16(plo, vb, acc[dg]);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -282,8 +316,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #define SKV_DEC_TARGET_BLOCKS 4096
 #endif
 
-void decode_plan(int64_t n_units, int64_t n_rows, int32_t* n_sub, int32_t* n_chunks) {
-  const int64_t subs = (n_rows + kDecSub - 1) / kDecSub;  // sub-chunks per unit
+void decode_plan(int dtype, int64_t n_units, int64_t n_rows, int32_t* n_sub, int32_t* n_chunks) {
+  const int64_t sub_keys = dtype == 0 ? DecGeom<float, 64>::kSubKeys : DecGeom<bf16_t, 64>::kSubKeys;
+  const int64_t subs = (n_rows + sub_keys - 1) / sub_keys;  // sub-chunks per unit
   int64_t ns = n_units * subs / SKV_DEC_TARGET_BLOCKS;
   ns = ns < 1 ? 1 : (ns > 64 ? 64 : ns);
   if (ns > subs) ns = subs;
@@ -293,24 +328,25 @@ void decode_plan(int64_t n_units, int64_t n_rows, int32_t* n_sub, int32_t* n_chu
 }
 int decode_max_group() { return kDecMaxGroup; }
 
-hipError_t launch_decode_attention(int head_dim, const DecodeArgs& a, hipStream_t s) {
+template <typename T, int D>
+static hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks)), block(kDecThreads);
-  if (head_dim == 128) {
-    decode_attention_kernel<128><<<grid, block, DecGeom<128>::kLds, s>>>(a);
-    if (a.n_chunks > 1) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      decode_combine_kernel<128><<<dim3((unsigned)a.n_units), dim3(256), 0, s>>>(a);
-    }
-  } else {
-    decode_attention_kernel<64><<<grid, block, DecGeom<64>::kLds, s>>>(a);
-    if (a.n_chunks > 1) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      decode_combine_kernel<64><<<dim3((unsigned)a.n_units), dim3(256), 0, s>>>(a);
-    }
+  constexpr int lds = DecGeom<T, D>::kLds;  // fp32 at head_dim 128 needs more than the default 64 KB
+  hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_attention_kernel<T, D>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e0 != hipSuccess) return e0;
+  decode_attention_kernel<T, D><<<grid, block, lds, s>>>(a);
+  if (a.n_chunks > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    decode_combine_kernel<D><<<dim3((unsigned)a.n_units), dim3(256), 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_attention(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s) {
+  if (dtype == 0) return head_dim == 128 ? launch_dec<float, 128>(a, s) : launch_dec<float, 64>(a, s);
+  return head_dim == 128 ? launch_dec<bf16_t, 128>(a, s) : launch_dec<bf16_t, 64>(a, s);
 }
 
 }  // namespace skv

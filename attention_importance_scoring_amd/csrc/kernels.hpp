@@ -110,8 +110,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 // Decode attention: units u = (layer, cache head); each unit's `group`
 // query heads attend over its first n_rows cached rows.
 struct DecodeArgs {
-  const void* q;              // [layers * q_heads_per_layer][D] (bf16)
-  const void* k;              // [n_units][head_stride] (bf16)
+  const void* q;              // [layers * q_heads_per_layer][D] (cache dtype)
+  const void* k;              // [n_units][head_stride] (bf16 or fp32)
   const void* v;
   int64_t head_stride;        // elements between cache head slabs
   int64_t n_rows;             // attended rows per head
@@ -126,8 +126,8 @@ struct DecodeArgs {
   float2* part_ml;            // n_chunks > 1: [n_units][n_chunks][16] (max, sum) in log2 units
   float* part_acc;            // n_chunks > 1: [n_units][n_chunks][16][D]
 };
-void decode_plan(int64_t n_units, int64_t n_rows, int32_t* n_sub, int32_t* n_chunks);
+void decode_plan(int dtype, int64_t n_units, int64_t n_rows, int32_t* n_sub, int32_t* n_chunks);
 int decode_max_group();
-hipError_t launch_decode_attention(int head_dim, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_attention(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace skv

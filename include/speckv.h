@@ -195,8 +195,8 @@ skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const voi
  * per_query_head), n_in rows allocated per head.  After out-of-place
  * compaction pass n_in = n_rows = n_keep; after in-place compaction the
  * prefill shape and n_rows = n_keep.  n_window, n_lookahead and aggregation
- * are ignored.  bf16 only (SKV_ERR_DTYPE); G <= 16 (SKV_ERR_SHAPE).
- * Inputs : q bf16 [n_layers][n_q_heads][head_dim]; k, v as above.
+ * are ignored.  bf16 or fp32 (the shape's dtype); G <= 16 (SKV_ERR_SHAPE).
+ * Inputs : q [n_layers][n_q_heads][head_dim] in the cache dtype; k, v as above.
  * Output : out float [n_layers][n_q_heads][head_dim].
  * Requires 1 <= n_rows <= n_in (SKV_ERR_PARAM).  Long caches are split over
  * several blocks per head, whose partial results go to the workspace;

@@ -223,7 +223,7 @@ def test_decode_validation(lib):
     assert dec(s, 0, q, k, v, out, None, 0) == PARAM
     assert dec(s, 289, q, k, v, out, None, 0) == PARAM
     assert dec(s, 288, None, k, v, out, None, 0) == NULL
-    assert dec(shape(n_in=288, n_window=16, dtype=skv.SKV_F32), 288, q, k, v, out, None, 0) == DTYPE
+    assert dec(shape(n_in=288, n_window=16, dtype=7), 288, q, k, v, out, None, 0) == DTYPE
     assert dec(shape(n_in=288, n_window=16, n_q_heads=34, n_kv_heads=2), 288, q, k, v, out, None, 0) == SHAPE  # G 17
     assert dec(s, 288, P((1 << 30) + 2), k, v, out, None, 0) == ALIGN
     assert dec(s, 288, q, k, v, P((2 << 30) + 64), None, 0) == ALIAS  # output inside the K cache
@@ -233,6 +233,11 @@ def test_decode_validation(lib):
     long = shape(n_in=4096, n_window=16)
     assert lib.speckv_decode_workspace_bytes(ctypes.byref(long), 4096, ctypes.byref(n)) == OK
     assert n.value >= 2 * 2 * 8 * 16 * (8 + 128 * 4)  # layers x KV heads x chunks x 16 slots x (max, sum, acc)
+    # fp32 caches are walked in 256-key sub-chunks: twice the chunks of bf16 at this size
+    n32 = ctypes.c_size_t(0)
+    long32 = shape(n_in=4096, n_window=16, dtype=skv.SKV_F32)
+    assert lib.speckv_decode_workspace_bytes(ctypes.byref(long32), 4096, ctypes.byref(n32)) == OK
+    assert n32.value >= 2 * n.value - 4096
     assert dec(long, 4096, q, k, v, out, None, 0) == WS
     assert dec(long, 4096, q, k, v, out, ws, n.value - 1) == WS
     assert lib.speckv_decode_workspace_bytes(ctypes.byref(long), 0, ctypes.byref(n)) == PARAM

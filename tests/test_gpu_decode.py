@@ -2,11 +2,12 @@
 ABI, against the fp64 oracle (oracle/decode.py).
 
 Tolerance, per output component: |gpu - oracle| <= 2e-4 * sum_j P_j |v_j|
-(oracle.error_scale).  The kernel's bf16 x bf16 products are exact and
-accumulate in fp32 over the head dim (a logit error of at most
-d * 2^-24 * sum |q_c k_c| * scale, under 6e-5 for the N(0, 1) inputs here),
-exp2 is correct to about one ulp, P enters the P V product as two bf16 terms
-(relative error at most 2^-18) and the sums over rows run in fp32: each
+(oracle.error_scale).  The kernel's bf16 x bf16 products are exact (fp32
+products round once) and accumulate in fp32 over the head dim (a logit
+error of at most d * 2^-24 * sum |q_c k_c| * scale, under 6e-5 for the
+N(0, 1) inputs here), exp2 is correct to about one ulp, P enters the P V
+product as two bf16 terms (relative error at most 2^-18; exact for fp32
+caches) and the sums over rows run in fp32: each
 probability is off by well under 1e-4 relative, which moves an output
 component by at most twice that in units of sum_j P_j |v_j|.
 """
@@ -25,11 +26,11 @@ pytestmark = pytest.mark.gpu
 DECODE_TOL = 2e-4
 
 
-def _cache(L, H, n_alloc, d, seed, device="cuda", scale_k=1.0, stride=None):
+def _cache(L, H, n_alloc, d, seed, device="cuda", scale_k=1.0, stride=None, dtype=torch.bfloat16):
     g = torch.Generator(device="cpu").manual_seed(seed)
     stride = n_alloc * d if stride is None else stride
-    kb = torch.randn((L, H, stride), generator=g).mul_(scale_k).to(torch.bfloat16)
-    vb = torch.randn((L, H, stride), generator=g).to(torch.bfloat16)
+    kb = torch.randn((L, H, stride), generator=g).mul_(scale_k).to(dtype)
+    vb = torch.randn((L, H, stride), generator=g).to(dtype)
     return kb.to(device), vb.to(device)
 
 
@@ -52,21 +53,28 @@ def _check(got, q, k, v, n_rows, what):
     return float(np.max(err / es))
 
 
-@pytest.mark.parametrize("L,Hq,Hkv,d,n_alloc,n_rows,pqh", [
-    (2, 8, 2, 128, 300, 300, 0),      # ragged single chunk, G 4
-    (1, 40, 8, 128, 288, 288, 0),     # the compacted 64K Qwen-shaped cache: G 5, 288 rows
-    (2, 14, 2, 64, 2049, 2049, 0),    # d 64, G 7, five chunks with a one-row tail
-    (1, 8, 8, 128, 40, 40, 0),        # G 1, two tiles: two of four waves idle
-    (2, 8, 2, 128, 1000, 288, 0),     # rows attended < rows allocated (in-place compacted layout)
-    (1, 16, 1, 64, 600, 517, 0),      # G 16 (the MFMA width), a 5-row second chunk
-    (2, 8, 2, 128, 200, 200, 1),      # one cache per query head
+@pytest.mark.parametrize("L,Hq,Hkv,d,n_alloc,n_rows,pqh,dt", [
+    (2, 8, 2, 128, 300, 300, 0, "bf16"),      # ragged single chunk, G 4
+    (1, 40, 8, 128, 288, 288, 0, "bf16"),     # the compacted 64K Qwen-shaped cache: G 5, 288 rows
+    (2, 14, 2, 64, 2049, 2049, 0, "bf16"),    # d 64, G 7, five chunks with a one-row tail
+    (1, 8, 8, 128, 40, 40, 0, "bf16"),        # G 1, two tiles: two of four waves idle
+    (2, 8, 2, 128, 1000, 288, 0, "bf16"),     # rows attended < rows allocated (in-place compacted layout)
+    (1, 16, 1, 64, 600, 517, 0, "bf16"),      # G 16 (the MFMA width), a 5-row second chunk
+    (2, 8, 2, 128, 200, 200, 1, "bf16"),      # one cache per query head
+    (2, 8, 2, 128, 300, 300, 0, "f32"),       # fp32: ragged, two 256-key chunks
+    (1, 4, 1, 64, 288, 288, 0, "f32"),        # fp32 d 64: the compacted tiny fp32 cache (G 4)
+    (2, 14, 2, 64, 2049, 2049, 0, "f32"),     # fp32 d 64, G 7, nine chunks with a one-row tail
+    (1, 16, 1, 128, 600, 517, 0, "f32"),      # fp32 G 16, rows attended < allocated
+    (2, 8, 2, 128, 200, 200, 1, "f32"),       # fp32, one cache per query head
 ])
-def test_decode_small(L, Hq, Hkv, d, n_alloc, n_rows, pqh):
+def test_decode_small(L, Hq, Hkv, d, n_alloc, n_rows, pqh, dt):
     H = Hq if pqh else Hkv
-    print(f"\n[case] L={L} Hq={Hq} H={H} d={d} rows {n_rows} of {n_alloc}", flush=True)
-    kb, vb = _cache(L, H, n_alloc, d, seed=n_rows + d)
-    q = torch.randn((L, Hq, d), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
-    shape = skv.make_shape(L, Hq, Hkv, d, n_alloc, 0, 0, skv.SKV_BF16, per_query_head=pqh)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    print(f"\n[case] {dt} L={L} Hq={Hq} H={H} d={d} rows {n_rows} of {n_alloc}", flush=True)
+    kb, vb = _cache(L, H, n_alloc, d, seed=n_rows + d, dtype=tdt)
+    q = torch.randn((L, Hq, d), generator=torch.Generator().manual_seed(3)).to(tdt).cuda()
+    shape = skv.make_shape(L, Hq, Hkv, d, n_alloc, 0, 0, skv.SKV_F32 if dt == "f32" else skv.SKV_BF16,
+                           per_query_head=pqh)
     got = _decode(shape, n_rows, q, kb, vb, L, Hq, d)
     k = np64(kb.view(L, H, n_alloc, d))
     v = np64(vb.view(L, H, n_alloc, d))
@@ -143,12 +151,13 @@ def test_qwen32b_shape_full_layers_sampled(n_rows):
                f"layer {layer} head {h}")
 
 
-@pytest.mark.parametrize("direction", ["rising", "falling"])
-def test_running_maximum_across_sub_chunks(direction):
+@pytest.mark.parametrize("direction,dt", [("rising", "bf16"), ("falling", "bf16"), ("rising", "f32")])
+def test_running_maximum_across_sub_chunks(direction, dt):
     # logits that rise (or fall) along the cache: with many heads each block walks
     # several sub-chunks and its running maximum changes in every one of them
     L, Hq, Hkv, d, n = 64, 16, 8, 64, 9000
-    print(f"\n[case] {direction} logits, {L * Hkv} heads x {n} rows", flush=True)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    print(f"\n[case] {direction} logits {dt}, {L * Hkv} heads x {n} rows", flush=True)
     g = torch.Generator(device="cuda").manual_seed(21)
     u = torch.randn(d, generator=g, device="cuda")
     u = u / u.norm()
@@ -156,10 +165,10 @@ def test_running_maximum_across_sub_chunks(direction):
     if direction == "falling":
         ramp = ramp.flip(0)
     k = 40.0 * ramp[None, None, :, None] * u + 0.5 * torch.randn((L, Hkv, n, d), generator=g, device="cuda")
-    kb = k.to(torch.bfloat16).reshape(L, Hkv, n * d)
-    vb = torch.randn((L, Hkv, n * d), generator=g, device="cuda").to(torch.bfloat16)
-    q = (u[None, None, :] + 0.1 * torch.randn((L, Hq, d), generator=g, device="cuda")).to(torch.bfloat16)
-    shape = skv.make_shape(L, Hq, Hkv, d, n, 0, 0, skv.SKV_BF16)
+    kb = k.to(tdt).reshape(L, Hkv, n * d)
+    vb = torch.randn((L, Hkv, n * d), generator=g, device="cuda").to(tdt)
+    q = (u[None, None, :] + 0.1 * torch.randn((L, Hq, d), generator=g, device="cuda")).to(tdt)
+    shape = skv.make_shape(L, Hq, Hkv, d, n, 0, 0, skv.SKV_F32 if dt == "f32" else skv.SKV_BF16)
     got = _decode(shape, n, q, kb, vb, L, Hq, d)
     for layer, h in [(0, 0), (40, 3), (63, 7)]:
         kk = np64(kb[layer:layer + 1, h:h + 1].view(1, 1, n, d))
