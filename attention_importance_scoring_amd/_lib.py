@@ -47,8 +47,7 @@ def load(path: str | None = None):
         return _LIB
     p = path or LIB_PATH
     if not os.path.exists(p):
-        raise RuntimeError(f"HIP library {p} is not built; run __graft_entry__.build() "
-                           "(python -m attention_importance_scoring_amd.build)")
+        raise RuntimeError(f"HIP library {p} is not built; run python -m attention_importance_scoring_amd.build")
     lib = ctypes.CDLL(p)
     S = ctypes.POINTER(Shape)
     lib.speckv_status_string.restype = ctypes.c_char_p

@@ -14,8 +14,8 @@ Two modes, both reading the CSV files rocprofv3 writes with
   for ``bench.py`` together with a hash of the kernel sources, so that a
   later change of the kernels voids it.
 
-    python -m attention_importance_scoring_amd.counters --stats gpurun_out/trace --title "..." --command "..."
-    python -m attention_importance_scoring_amd.counters --fetch gpurun_out/pmc_fetch --write gpurun_out/pmc_write \\
+    python -m attention_importance_scoring_amd.counters --stats out/trace --title "..." --command "..."
+    python -m attention_importance_scoring_amd.counters --fetch out/pmc_fetch --write out/pmc_write \\
         --calib-mib 1024 --workload qwen32b_shape_64k --command "..." \\
         --out profiles/speckv_kernels_qwen32b_shape_64k_traffic.json
 """

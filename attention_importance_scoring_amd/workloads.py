@@ -109,14 +109,16 @@ class SpecPCConfig:
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
 
-CONFIGS = {
-    1: SpecKVConfig("tiny_fp32_2k", 1, 4, 1, 64, "f32", 2048, 32, 16, 256, 7, "normal", "fixed8", 3.0),
-    2: SpecKVConfig("llama8b_shape_16k", 32, 32, 8, 128, "bf16", 16384, 32, 64, 1024, 7, "normal", "one_percent", 2.5),
-    3: SpecKVConfig("qwen32b_shape_64k", 64, 40, 8, 128, "bf16", 65536, 32, 128, 256, 7, "lowrank8", "one_percent", 2.5),
-    4: SpecKVConfig("llama8b_shape_128k_inplace", 32, 32, 8, 128, "bf16", 131072, 64, 256, 2048, 7, "mixture", "none", 0.0,
-                    in_place=True),
-    5: SpecPCConfig("specpc_draft_32k", 24, 14, 2, 64, "bf16", 32768, 512, 1, 4, 2048, 7, 2.5),
-}
+TINY_FP32_2K = SpecKVConfig("tiny_fp32_2k", 1, 4, 1, 64, "f32", 2048, 32, 16, 256, 7, "normal", "fixed8", 3.0)
+LLAMA8B_16K = SpecKVConfig("llama8b_shape_16k", 32, 32, 8, 128, "bf16", 16384, 32, 64, 1024, 7, "normal",
+                           "one_percent", 2.5)
+QWEN32B_64K = SpecKVConfig("qwen32b_shape_64k", 64, 40, 8, 128, "bf16", 65536, 32, 128, 256, 7, "lowrank8",
+                           "one_percent", 2.5)
+LLAMA8B_128K_INPLACE = SpecKVConfig("llama8b_shape_128k_inplace", 32, 32, 8, 128, "bf16", 131072, 64, 256, 2048, 7,
+                                    "mixture", "none", 0.0, in_place=True)
+SPECPC_DRAFT_32K = SpecPCConfig("specpc_draft_32k", 24, 14, 2, 64, "bf16", 32768, 512, 1, 4, 2048, 7, 2.5)
+
+WORKLOADS = {c.name: c for c in (TINY_FP32_2K, LLAMA8B_16K, QWEN32B_64K, LLAMA8B_128K_INPLACE, SPECPC_DRAFT_32K)}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -137,7 +139,7 @@ class CascadeConfig:
 
 CASCADES = {
     "speckv_pc_cascade_32k": CascadeConfig(
-        "speckv_pc_cascade_32k", CONFIGS[5],
+        "speckv_pc_cascade_32k", SPECPC_DRAFT_32K,
         SpecKVConfig("qwen32b_shape_32k_target", 64, 40, 8, 128, "bf16", 32768, 32, 128, 256, 7, "lowrank8",
                      "one_percent", 2.5)),
 }

@@ -460,9 +460,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    cfg = {c.name: c for c in wl.CONFIGS.values()}.get(args.workload)
+    cfg = wl.WORKLOADS.get(args.workload)
     if args.workload == "decode_qwen32b_shape_64k":
-        cfg = wl.CONFIGS[3]
+        cfg = wl.QWEN32B_64K
         out, inp = bench_decode(args, cfg, torch, skv, wl)
     elif args.workload in wl.CASCADES:
         out, inp = bench_cascade(args, wl.CASCADES[args.workload], torch, skv, wl)
@@ -482,7 +482,7 @@ def main():
     if not args.no_cpu_baseline and args.workload == "decode_qwen32b_shape_64k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = decode_cpu_baseline(cfg, inp, args.decode_cache)
-    elif not args.no_cpu_baseline and args.workload in {c.name for c in wl.CONFIGS.values()} \
+    elif not args.no_cpu_baseline and args.workload in wl.WORKLOADS \
             and args.workload != "specpc_draft_32k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = speckv_cpu_baseline(cfg, inp)

@@ -114,7 +114,7 @@ def test_peaked_and_flat_logits():
 def test_decode_over_the_compacted_cache_of_the_speckv_path():
     # scores -> select -> compact on the GPU, then decode over the compacted cache:
     # equals attention over the GPU's kept rows of the full cache
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=2, n_in=3000, C_max=100)
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_in=3000, C_max=100)
     print(f"\n[case] {cfg.name} reduced: n_in {cfg.n_in}, C_max {cfg.C_max}", flush=True)
     inp = wl.speckv_inputs(cfg, 12, "cuda")
     res = run_speckv(cfg, inp)

@@ -54,7 +54,7 @@ def _check_sampled_units(scores, pooled, kept, q_obs, k, cfg, units):
 
 
 def test_qwen32b_shape_64k_all_layers_one_call():
-    cfg = wl.CONFIGS[3]
+    cfg = wl.QWEN32B_64K
     print(f"\n[case] {cfg.name}: 64 layers in one call, n_in={cfg.n_in}, seed 3 on the GPU", flush=True)
     inp = wl.speckv_inputs(cfg, 3, "cuda")  # the inputs bench.py times
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
@@ -77,7 +77,7 @@ def test_qwen32b_shape_64k_all_layers_one_call():
 
 
 def test_llama8b_shape_128k_in_place_one_layer_per_call():
-    cfg = wl.CONFIGS[4]
+    cfg = wl.LLAMA8B_128K_INPLACE
     layers = [0, 31]
     print(f"\n[case] {cfg.name}: layers {layers} one per call, in place, n_in={cfg.n_in}", flush=True)
     inp = wl.speckv_inputs(cfg, 4, "cuda", layers=layers)
@@ -106,7 +106,7 @@ def test_llama8b_shape_128k_in_place_one_layer_per_call():
 
 
 def test_specpc_draft_32k_full_stack_one_call():
-    cfg = wl.CONFIGS[5]
+    cfg = wl.SPECPC_DRAFT_32K
     print(f"\n[case] {cfg.name}: {cfg.n_layers} layers (l_skip {cfg.l_skip}), n_in={cfg.n_in}, W={cfg.window}",
           flush=True)
     inp = wl.specpc_inputs(cfg, 5, "cuda")  # the inputs bench.py times
@@ -132,7 +132,7 @@ def test_specpc_draft_32k_full_stack_one_call():
 def test_many_long_units_four_key_tiles_per_wave(dtype, d):
     # 768 units of 16K keys: every block walks at least 16 groups of resident
     # keys, which is where the planner holds four key tiles per wave.
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=96, n_q_heads=8, n_kv_heads=8, head_dim=d, dtype=dtype,
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=96, n_q_heads=8, n_kv_heads=8, head_dim=d, dtype=dtype,
                      n_in=16384 + 8, n_window=8, n_lookahead=4, C_max=200)
     print(f"\n[case] {cfg.n_layers * cfg.n_kv_heads} units, {dtype} d={d}, n_in={cfg.n_in}", flush=True)
     inp = wl.speckv_inputs(cfg, 31, "cuda")

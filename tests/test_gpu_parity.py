@@ -63,8 +63,8 @@ def _full_check(cfg, seed, C_max=None, pool_kernel=None, kv_head_stride=None, po
     return out
 
 
-def test_config1_tiny_fp32_full():
-    _full_check(wl.CONFIGS[1], seed=1)
+def test_tiny_fp32_2k_full():
+    _full_check(wl.TINY_FP32_2K, seed=1)
 
 
 @pytest.mark.parametrize("case", [
@@ -76,30 +76,30 @@ def test_config1_tiny_fp32_full():
     dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_in=300, n_window=20, n_lookahead=3, C_max=0),
 ], ids=["ragged-bf16-d128", "gqa7-d64", "window-only", "mha-cmax-npre", "cmax-above-npre", "cmax-zero"])
 def test_small_bf16_shapes(case):
-    cfg = wl.reduced(wl.CONFIGS[2], **case)
+    cfg = wl.reduced(wl.LLAMA8B_16K, **case)
     _full_check(cfg, seed=11)
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64)])
 def test_other_dtype_headdim_combinations(dtype, d):
-    cfg = wl.reduced(wl.CONFIGS[1], dtype=dtype, head_dim=d, n_in=1100, n_q_heads=6, n_kv_heads=2)
+    cfg = wl.reduced(wl.TINY_FP32_2K, dtype=dtype, head_dim=d, n_in=1100, n_q_heads=6, n_kv_heads=2)
     _full_check(cfg, seed=3)
 
 
 def test_padded_head_stride_and_avg_pool():
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=2, n_in=900, C_max=77)
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_in=900, C_max=77)
     _full_check(cfg, seed=4, kv_head_stride=900 * 128 + 64, pool="avg", pool_kernel=5)
 
 
 def test_no_pooling():
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=1, n_in=1200, C_max=90)
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=1, n_in=1200, C_max=90)
     _full_check(cfg, seed=5, pool="none", pool_kernel=1)
 
 
 def test_exact_ties_take_lowest_index():
     # identical key rows give bit-identical scores; with no pooling the cut falls inside
     # the tie and both sides must keep the lowest indices.
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=1, n_kv_heads=1, n_q_heads=4, n_in=600, n_window=16, n_lookahead=16,
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=1, n_kv_heads=1, n_q_heads=4, n_in=600, n_window=16, n_lookahead=16,
                      C_max=40, heavy_hitters="none")
     host = wl.speckv_inputs(cfg, 6, "cpu")
     kb = host["k_buf"].view(1, 1, 600, 128)
@@ -125,7 +125,7 @@ _MANY_UNITS = dict(n_layers=32, n_q_heads=8, n_kv_heads=8, n_in=8200, n_window=8
 
 
 def test_many_units_revisited_rows():
-    _full_check(wl.reduced(wl.CONFIGS[2], **_MANY_UNITS), seed=12)
+    _full_check(wl.reduced(wl.LLAMA8B_16K, **_MANY_UNITS), seed=12)
 
 
 @pytest.mark.parametrize("late", [True, False], ids=["jump-up", "jump-down"])
@@ -133,7 +133,7 @@ def test_logit_jumps_between_key_groups(late):
     # Keys in one half of every aligned 1024-key block get a logit boost of
     # about 75 (log2 units): rows first meet small logits and later ones
     # beyond 2^64 of their reference (jump-up), or the reverse (jump-down).
-    cfg = wl.reduced(wl.CONFIGS[2], heavy_hitters="none", **_MANY_UNITS)
+    cfg = wl.reduced(wl.LLAMA8B_16K, heavy_hitters="none", **_MANY_UNITS)
     host = wl.speckv_inputs(cfg, 13, "cpu")
     d, n_in = cfg.head_dim, cfg.n_in
     u = torch.ones(d) / math.sqrt(d)
@@ -159,7 +159,7 @@ def test_logit_jumps_between_key_groups(late):
 def test_aggregation_and_per_query_head_variants(agg, pqh):
     # G * n_obs = 520 rows: two row parts per KV head, so the max aggregation
     # also crosses the part combine.
-    cfg = wl.reduced(wl.CONFIGS[2], n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=3000, n_window=40, n_lookahead=90,
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=3000, n_window=40, n_lookahead=90,
                      C_max=150)
     print(f"\n[case] aggregation {agg}, per_query_head {pqh}", flush=True)
     host = wl.speckv_inputs(cfg, 17, "cpu")
@@ -191,7 +191,7 @@ def test_aggregation_and_per_query_head_variants(agg, pqh):
 
 
 def test_in_place_equals_out_of_place_and_deterministic():
-    cfg = wl.reduced(wl.CONFIGS[4], n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
+    cfg = wl.reduced(wl.LLAMA8B_128K_INPLACE, n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
     host = wl.speckv_inputs(cfg, 7, "cpu")
     a = run_speckv(cfg, _to(host, "cuda"))
     b = run_speckv(cfg, _to(host, "cuda"))
@@ -205,9 +205,9 @@ def test_in_place_equals_out_of_place_and_deterministic():
     assert_compacted(c["k_c"], c["v_c"], k0, v0, c["kept"])
 
 
-def test_config2_llama_shape_two_layers_full_length():
-    cfg = wl.CONFIGS[2]
-    print("\n[case] config 2, layers 0 and 31, n_in=16384", flush=True)
+def test_llama8b_shape_16k_two_layers_full_length():
+    cfg = wl.LLAMA8B_16K
+    print("\n[case] llama8b_shape_16k, layers 0 and 31, n_in=16384", flush=True)
     host = wl.speckv_inputs(cfg, 2, "cpu", layers=[0, 31])
     inp = _to(host, "cuda")
     red = wl.reduced(cfg, n_layers=2)
@@ -260,20 +260,20 @@ def _specpc_check(cfg, seed, weights=None):
 ], ids=["ragged", "single-window-row", "window-equals-input", "d128-group-over-two-stages", "lookahead-8",
         "window-of-draft-rows", "lookahead-past-window-d128"])
 def test_specpc_small(case):
-    _specpc_check(wl.reduced(wl.CONFIGS[5], **case), seed=21)
+    _specpc_check(wl.reduced(wl.SPECPC_DRAFT_32K, **case), seed=21)
 
 
 def test_specpc_user_weights_and_fp32():
-    cfg = wl.reduced(wl.CONFIGS[5], n_layers=2, l_skip=1, n_in=640, window=70, k_top=50, dtype="f32")
+    cfg = wl.reduced(wl.SPECPC_DRAFT_32K, n_layers=2, l_skip=1, n_in=640, window=70, k_top=50, dtype="f32")
     w = np.random.default_rng(0).random(70) + 0.05
     _specpc_check(cfg, seed=22, weights=w)
 
 
-def test_specpc_config5_two_used_layers_full_length():
+def test_specpc_draft_32k_two_used_layers_full_length():
     # full n_in and W of the draft workload with 2 of the 20 used layers
-    _specpc_check(wl.reduced(wl.CONFIGS[5], n_layers=6), seed=5)
+    _specpc_check(wl.reduced(wl.SPECPC_DRAFT_32K, n_layers=6), seed=5)
 
 
-def test_specpc_config5_lookahead_16_two_used_layers():
+def test_specpc_draft_32k_lookahead_16_two_used_layers():
     # the draft workload with 16 lookahead tokens: 15 draft rows end the window
-    _specpc_check(wl.reduced(wl.CONFIGS[5], n_layers=6, n_lookahead=16), seed=6)
+    _specpc_check(wl.reduced(wl.SPECPC_DRAFT_32K, n_layers=6, n_lookahead=16), seed=6)

@@ -169,7 +169,7 @@ def test_bruteforce_fsum_tiny(seed):
 
 def test_planted_heavy_hitters_recovered_tiny_config():
     from attention_importance_scoring_amd import workloads as w
-    cfg = w.CONFIGS[1]
+    cfg = w.TINY_FP32_2K
     inp = w.speckv_inputs(cfg, seed=1)
     q = w.to_numpy_f64(inp["q_obs"])
     k = w.to_numpy_f64(inp["k"])

@@ -9,7 +9,7 @@ from attention_importance_scoring_amd import workloads as w
 
 
 def test_same_seed_same_bytes_and_shapes():
-    cfg = w.reduced(w.CONFIGS[2], n_layers=2, n_in=512, C_max=64)
+    cfg = w.reduced(w.LLAMA8B_16K, n_layers=2, n_in=512, C_max=64)
     a = w.speckv_inputs(cfg, seed=2)
     b = w.speckv_inputs(cfg, seed=2)
     c = w.speckv_inputs(cfg, seed=3)
@@ -21,7 +21,7 @@ def test_same_seed_same_bytes_and_shapes():
 
 
 def test_padded_head_stride_views():
-    cfg = w.reduced(w.CONFIGS[1], n_in=300)
+    cfg = w.reduced(w.TINY_FP32_2K, n_in=300)
     a = w.speckv_inputs(cfg, seed=1)
     b = w.speckv_inputs(cfg, seed=1, kv_head_stride=300 * 64 + 40)
     assert torch.equal(a["k"], b["k"]) and b["k_buf"].shape[-1] == 300 * 64 + 40
@@ -30,7 +30,7 @@ def test_padded_head_stride_views():
 def test_one_percent_heavy_hitters_are_recovered_llama_layer():
     # One layer of the Llama-3.1-8B-shaped 16K workload: every kept prefix key lies
     # within the pooling half-width of a planted key (or the sink).
-    cfg = w.CONFIGS[2]
+    cfg = w.LLAMA8B_16K
     inp = w.speckv_inputs(cfg, seed=2, layers=[0])
     q = w.to_numpy_f64(inp["q_obs"])
     k = w.to_numpy_f64(inp["k"])
@@ -46,7 +46,7 @@ def test_one_percent_heavy_hitters_are_recovered_llama_layer():
 
 
 def test_specpc_inputs_shapes():
-    cfg = w.CONFIGS[5]
+    cfg = w.SPECPC_DRAFT_32K
     small = w.dataclasses.replace(cfg, n_layers=5, n_in=1024, window=64)
     inp = w.specpc_inputs(small, seed=5)
     assert inp["q_win"].shape == (5, 14, 64, 64) and inp["k"].shape == (5, 2, 1024, 64)
