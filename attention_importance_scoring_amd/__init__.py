@@ -1,4 +1,5 @@
-"""MI355X (gfx950) SpecKV / SpecPC importance scoring and KV compaction.
+"""MI355X (gfx950) SpecKV / SpecPC importance scoring, KV compaction and
+decode attention over the compacted cache.
 
 Thin Python binding over the C ABI in include/speckv.h (libspeckv.so): the
 functions below carry the C names, turn torch device tensors into pointers

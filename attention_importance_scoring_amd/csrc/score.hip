@@ -6,11 +6,14 @@
 // Pass 1 (row statistics): for every query row r, the log2-domain
 //   lse_r = log2 sum_j 2^(c * <q_r, k_j>),  c = scale * log2(e),
 // built from per-block (max, sum) partials so that the score matrix is never
-// stored.  Pass 2 (column sums): score_j = sum_r 2^(c * <q_r, k_j> - lse_r).
+// stored.  Pass 2 (column sums): score_j = sum_r 2^(c * <q_r, k_j> - lse_r)
+// (or the maximum over r, in the max-aggregation variant).
 //
-// Work split: one 8-wave block per CU owns a chunk of consecutive keys of one
-// unit (layer, KV head) and one "part" of the unit's query rows: as many
-// 32-row tiles as fit in LDS (up to ~150 KB), copied there once.  The parts
+// Work split: one block per CU (8 waves; 12 at head_dim 64, where the vector
+// work dominates) owns a chunk of consecutive keys of one unit (layer, KV
+// head, or query head when each has its own kept set) and one "part" of the
+// unit's query rows: as many 32-row tiles as fit in LDS (up to ~156 KB),
+// copied there once.  The parts
 // of a chunk are neighbouring blocks on one XCD, so K comes from HBM about
 // once and from L2 for the other parts; pass 2 writes one column-sum row per
 // part and a small kernel adds them in part order.  Every wave walks its

@@ -12,8 +12,12 @@
  *     draft's attention activations over a window of queries with weights
  *     that fall away from the end, skipping the first l_skip layers, mean
  *     first and then max;
+ *   - section "Key designs", SpecKV-PC paragraph: SpecPC first cuts the
+ *     prompt, then SpecKV cuts the target's cache over the shorter prompt;
  *   - section "Loss / training strategy": local pooling keeps the kept
- *     tokens contiguous.
+ *     tokens contiguous;
+ *   - section "Background": attention compute and KV-cache memory grow with
+ *     the context, which decode attention over the compacted cache saves.
  *
  * Conventions shared by every entry point
  *   - All buffer pointers are DEVICE pointers owned by the caller, including
