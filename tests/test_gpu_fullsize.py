@@ -149,3 +149,56 @@ def test_many_long_units_four_key_tiles_per_wave(dtype, d):
     sc, pl, kp = scores.cpu().numpy(), pooled.cpu().numpy(), kept.cpu().numpy()
     _check_every_unit(sc, pl, kp, cfg)
     _check_sampled_units(sc, pl, kp, inp["q_obs"], inp["k"], cfg, [(0, 0), (47, 3), (95, 7)])
+
+
+@pytest.mark.parametrize("aggregation,per_query_head", [("max", False), ("sum", True)],
+                         ids=["max-per-kv-head", "sum-per-query-head"])
+def test_qwen32b_shape_64k_variants_one_call(aggregation, per_query_head):
+    # the bench's --aggregation max and --per-query-head launches on the same inputs
+    cfg = wl.QWEN32B_64K
+    print(f"\n[case] {cfg.name} {aggregation} per_query_head={per_query_head}: 64 layers in one call", flush=True)
+    inp = wl.speckv_inputs(cfg, 3, "cuda")
+    L, Hq, Hkv, d, G = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.G
+    H = Hq if per_query_head else Hkv
+    shape = skv.make_shape(L, Hq, Hkv, d, cfg.n_in, cfg.n_window, cfg.n_lookahead, skv.SKV_BF16,
+                           kv_head_stride=inp["kv_head_stride"],
+                           aggregation=skv.SKV_AGG_MAX if aggregation == "max" else skv.SKV_AGG_SUM,
+                           per_query_head=int(per_query_head))
+    ws = workspace(shape, cfg.C_max)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    scores = torch.full((L, H, cfg.n_pre), float("nan"), dtype=torch.float32, device="cuda")
+    pooled = torch.full_like(scores, float("nan"))
+    kept = torch.full((L, H, n_keep), -1, dtype=torch.int32, device="cuda")
+    kc = torch.empty((L, H, n_keep, d), dtype=inp["k"].dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], scores, ws)
+    skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws)
+    skv.speckv_compact(shape, inp["k_buf"], inp["v_buf"], kept, n_keep, kc, vc, ws)
+    torch.cuda.synchronize()
+    # compacted rows: query head h's cache holds rows of KV head h // G
+    if per_query_head:
+        for g in range(G):  # query heads g, G + g, 2 G + g, ... read KV heads 0, 1, 2, ...
+            assert_compacted(kc[:, g::G], vc[:, g::G], inp["k"], inp["v"], kept[:, g::G])
+    else:
+        assert_compacted(kc, vc, inp["k"], inp["v"], kept)
+    sc = scores.cpu().numpy().astype(np.float64)
+    assert np.isfinite(sc).all() and (sc >= 0).all()
+    rows = cfg.n_obs * (1 if per_query_head else G)
+    if aggregation == "max":
+        assert (sc <= 1.0 + 1e-6).all()  # a maximum of probabilities
+    else:
+        np.testing.assert_allclose(sc.sum(-1), rows, rtol=1e-4)
+    pl, kp = pooled.cpu().numpy(), kept.cpu().numpy()
+    for u in range(0, L * H, 37):  # the selection rule on the GPU's own pooled scores, a spread of units
+        layer, h = divmod(u, H)
+        exact = oracle.select_kept(pl[layer, h].astype(np.float64), cfg.C_max, cfg.n_window)
+        assert (kp[layer, h] == exact).all(), f"unit {u}: selection differs from the rule on its own scores"
+    scale = oracle.default_scale(d)
+    for layer, h in [(0, 0), (29, 3), (63, H - 1)]:
+        print(f"[unit] layer {layer} head {h}", flush=True)
+        q = inp["q_obs"][layer, h:h + 1] if per_query_head else inp["q_obs"][layer, h * G:(h + 1) * G]
+        kvh = h // G if per_query_head else h
+        want = oracle.head_scores(np64(q), np64(inp["k"][layer, kvh])[:cfg.n_pre], scale, aggregation)
+        assert_scores_close(sc[layer, h], want, 1 if per_query_head else G, cfg.n_obs, f"scores[{layer},{h}]")
+        assert_kept_matches(kp[layer, h][None], pl[layer, h][None], oracle.pool1d(want, cfg.pool_kernel, "max")[None],
+                            cfg.C_max, cfg.n_window, f"kept[{layer},{h}]")
