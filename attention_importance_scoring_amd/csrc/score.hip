@@ -474,7 +474,8 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
 // ---------------------------------------------------------------------------
 
 template <typename T, int D, int KT>
-static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
+static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl,
+                     int64_t target_blocks = SKV_TARGET_BLOCKS) {
   using Gm = ScoreGeom<T, D, KT>;
   // Row parts: as many 32-row tiles as the LDS budget holds, split evenly.
   const int64_t tiles = (n_rows + 31) / 32;
@@ -493,10 +494,9 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
   // Key chunks: enough blocks (units x chunks x parts) for several rounds over
   // the 256 CUs, one block per CU; at most kMaxSubPerChunk groups of resident
   // keys per block, so the parts of a chunk stay close together in time.
-  constexpr int64_t kTargetBlocks = SKV_TARGET_BLOCKS;
   const int64_t subs = (n_keys + Gm::kKeysPerSub - 1) / Gm::kKeysPerSub;
   const int64_t ups = n_units * pl->n_parts;
-  int64_t chunks = (kTargetBlocks + ups - 1) / ups;
+  int64_t chunks = (target_blocks + ups - 1) / ups;
   chunks = chunks < 1 ? 1 : (chunks > subs ? subs : chunks);
   int64_t per = (subs + chunks - 1) / chunks;
   if (per > kMaxSubPerChunk) per = kMaxSubPerChunk;
@@ -507,14 +507,22 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
 
 // Four key tiles per wave halve the LDS reads of the row operand per MFMA,
 // but coarsen the key split: they are taken only where the resident-key
-// registers allow them and every block still walks many key groups.
+// registers allow them and every block still walks many key groups.  When
+// that needs fewer, longer blocks than the usual target, four tiles still
+// win as long as every CU gets a block (one round of blocks, no tail).
 template <typename T, int D>
 static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   plan_for<T, D, 2>(n_units, n_rows, n_keys, pl);
   if constexpr (4 * 4 * RowFrag<T, D>::kNV <= 128) {
+    constexpr int64_t kCUs = 256;
     ScorePlan p4;
     plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4);
-    if (p4.n_sub >= 16) *pl = p4;
+    if (p4.n_sub >= 16) {
+      *pl = p4;
+      return;
+    }
+    plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4, kCUs);
+    if (p4.n_sub >= 16 && n_units * p4.n_parts * p4.n_chunks >= kCUs) *pl = p4;
   }
 }
 
