@@ -236,8 +236,8 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
                          size_t ws_bytes, void* stream) {
   Dims d;
   SKV_TRY(check_shape(shape, &d));
-  if (!q_obs || !k || !scores) return SKV_ERR_NULL;
   const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
+  if (!q_obs || !k || (!scores && n_pre > 0)) return SKV_ERR_NULL;  // an empty prefix has no scores
   if (n_obs < 1) return SKV_ERR_SHAPE;
   if (d.group() * n_obs > kMaxRows) return SKV_ERR_SHAPE;
   if (!aligned(q_obs, 16) || !aligned(k, 16) || !aligned(scores, 4)) return SKV_ERR_ALIGN;
@@ -288,7 +288,7 @@ skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_
                          int32_t* kept, float* pooled, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   SKV_TRY(check_shape(shape, &d));
-  if (!scores || !kept) return SKV_ERR_NULL;
+  if (!kept || (!scores && d.n_in > d.n_window)) return SKV_ERR_NULL;  // an empty prefix has no scores
   if (C_max < 0) return SKV_ERR_PARAM;
   if (pool != SKV_POOL_NONE && pool != SKV_POOL_MAX && pool != SKV_POOL_AVG) return SKV_ERR_PARAM;
   if (pool != SKV_POOL_NONE && (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 4097)) return SKV_ERR_PARAM;

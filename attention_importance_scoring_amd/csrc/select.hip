@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
 
   if (MODE != kSelSegment)
     for (int t = tid; t < a.n_window; t += kSelThreads) kept[a.n_top + t] = n + t;
+  if (len <= 0) return;  // nothing to select (an empty prefix keeps the window only); block-uniform
 
   // 1. keys; key 0 marks padding (every non-negative score maps above 2^31)
   uint32_t key[E];

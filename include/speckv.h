@@ -114,7 +114,7 @@ skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out_n_k
  * Output : scores float [n_layers][H][n_pre] (raw sums total G or 1 times
  *          (n_window + n_lookahead) per head).
  * Requires n_window + n_lookahead >= 1 and G * (n_window + n_lookahead)
- * <= 2^20; n_pre = 0 is accepted and does nothing. */
+ * <= 2^20; n_pre = 0 is accepted and does nothing (scores may then be NULL). */
 skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
                          void* workspace, size_t workspace_bytes, void* stream);
 
@@ -124,7 +124,8 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
  * in-range mean; SKV_POOL_NONE copies); then the min(C_max, n_pre) best
  * prefix keys, ordered by pooled score descending and lower index first on
  * ties, plus every window key n_pre .. n_in - 1; written ascending.
- * Inputs : scores float [n_layers][H][n_pre] (non-negative).
+ * Inputs : scores float [n_layers][H][n_pre] (non-negative; NULL when
+ *          n_pre = 0, where the kept list is the window alone).
  * Outputs: kept int32 [n_layers][H][n_keep]; pooled float
  *          [n_layers][H][n_pre] or NULL.
  * The SpecPC token selection is this call on a shape with n_layers = 1,

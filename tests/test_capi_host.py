@@ -241,3 +241,13 @@ def test_decode_validation(lib):
     assert dec(long, 4096, q, k, v, out, None, 0) == WS
     assert dec(long, 4096, q, k, v, out, ws, n.value - 1) == WS
     assert lib.speckv_decode_workspace_bytes(ctypes.byref(long), 0, ctypes.byref(n)) == PARAM
+
+
+def test_empty_prefix_accepts_null_scores(lib):
+    # n_window = n_in: no scores exist, so a NULL scores pointer is valid; with a prefix it is not
+    s = shape(n_in=64, n_window=64)
+    q, k, ws = P(1 << 30), P(2 << 30), P(3 << 30)
+    assert lib.speckv_scores(ctypes.byref(s), q, k, None, ws, 1 << 20, None) == OK  # nothing to launch
+    sp = shape()
+    assert lib.speckv_scores(ctypes.byref(sp), q, k, None, ws, 1 << 30, None) == NULL
+    assert lib.speckv_select(ctypes.byref(sp), None, 16, 1, 7, P(4 << 30), None, ws, 1 << 30, None) == NULL

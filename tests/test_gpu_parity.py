@@ -67,6 +67,31 @@ def test_tiny_fp32_2k_full():
     _full_check(wl.TINY_FP32_2K, seed=1)
 
 
+@pytest.mark.parametrize("pooled_out", [False, True])
+def test_empty_prefix_keeps_the_window(pooled_out):
+    # n_window = n_in: nothing is scored (scores and pooled have no elements), the kept list is the
+    # whole window and compaction copies every row
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=48, n_window=48, n_lookahead=8,
+                     C_max=16, keys="normal", heavy_hitters="none")
+    print(f"\n[case] empty prefix: n_in = n_window = {cfg.n_in}, pooled output {pooled_out}", flush=True)
+    inp = wl.speckv_inputs(cfg, 41, "cuda")
+    shape = shape_of(cfg, kv_head_stride=inp["kv_head_stride"])
+    ws = workspace(shape, cfg.C_max)
+    n_keep = skv.speckv_n_keep(shape, cfg.C_max)
+    assert n_keep == cfg.n_in
+    scores = torch.empty((2, 2, 0), dtype=torch.float32, device="cuda")
+    pooled = torch.empty_like(scores) if pooled_out else None
+    kept = torch.full((2, 2, n_keep), -1, dtype=torch.int32, device="cuda")
+    kc = torch.empty((2, 2, n_keep, cfg.head_dim), dtype=inp["k"].dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], scores, ws)
+    skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, 7, kept, pooled, ws)
+    skv.speckv_compact(shape, inp["k_buf"], inp["v_buf"], kept, n_keep, kc, vc, ws)
+    torch.cuda.synchronize()
+    assert (kept.cpu() == torch.arange(cfg.n_in, dtype=torch.int32)).all()
+    assert torch.equal(kc, inp["k"]) and torch.equal(vc, inp["v"])
+
+
 @pytest.mark.parametrize("case", [
     dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_in=1000, n_window=7, n_lookahead=5, C_max=100),
     dict(n_layers=1, n_q_heads=14, n_kv_heads=2, head_dim=64, n_in=1537, n_window=33, n_lookahead=31, C_max=64),
