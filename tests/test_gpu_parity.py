@@ -99,7 +99,10 @@ def test_empty_prefix_keeps_the_window(pooled_out):
     dict(n_layers=1, n_q_heads=4, n_kv_heads=4, head_dim=64, n_in=513, n_window=1, n_lookahead=40, C_max=511),
     dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, n_in=300, n_window=20, n_lookahead=3, C_max=1000),
     dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_in=300, n_window=20, n_lookahead=3, C_max=0),
-], ids=["ragged-bf16-d128", "gqa7-d64", "window-only", "mha-cmax-npre", "cmax-above-npre", "cmax-zero"])
+    dict(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_in=33, n_window=32, n_lookahead=4, C_max=8),
+    dict(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=128, n_in=37, n_window=32, n_lookahead=4, C_max=2),
+], ids=["ragged-bf16-d128", "gqa7-d64", "window-only", "mha-cmax-npre", "cmax-above-npre", "cmax-zero",
+        "one-key-prefix", "prefix-shorter-than-pool"])
 def test_small_bf16_shapes(case):
     cfg = wl.reduced(wl.LLAMA8B_16K, **case)
     _full_check(cfg, seed=11)
