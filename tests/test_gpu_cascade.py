@@ -125,3 +125,27 @@ def test_cascade_full_size_sampled():
     exact = oracle.select_kept(out["ts_pooled"].cpu().numpy().astype(np.float64), cc.draft.k_top, 0)
     assert (out["tokens"].cpu().numpy() == exact).all()
     _check_stage2(out, inp, cc, [(0, 0), (31, 4), (63, 7)])
+
+
+def test_gather_tokens_ragged_list_and_out_of_range_tokens():
+    # any token list (repeats, any order) is gathered for every head; tokens outside [0, n_in) give zero rows
+    L, Hq, Hkv, d, n_in = 3, 8, 2, 64, 300
+    print(f"\n[case] gather tokens: {L} layers x {Hkv} heads, n_in {n_in}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(17)
+    stride = n_in * d + 64
+    kb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    vb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    tokens = torch.tensor([299, 0, 5, 5, 150, -1, 300, 77, 2**30], dtype=torch.int32, device="cuda")
+    n = tokens.numel()
+    shape = skv.make_shape(L, Hq, Hkv, d, n_in, 0, 0, skv.SKV_BF16, kv_head_stride=stride)
+    ko = torch.full((L, Hkv, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vo = torch.full_like(ko, float("nan"))
+    skv.specpc_gather_tokens(shape, kb, vb, tokens, n, ko, vo)
+    torch.cuda.synchronize()
+    k = kb[:, :, :n_in * d].unflatten(2, (n_in, d))
+    v = vb[:, :, :n_in * d].unflatten(2, (n_in, d))
+    for t, j in enumerate(tokens.tolist()):
+        if 0 <= j < n_in:
+            assert torch.equal(ko[:, :, t], k[:, :, j]) and torch.equal(vo[:, :, t], v[:, :, j])
+        else:
+            assert (ko[:, :, t] == 0).all() and (vo[:, :, t] == 0).all()
