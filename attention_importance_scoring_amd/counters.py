@@ -74,16 +74,21 @@ def stats_table(d: str) -> list[dict]:
     return rows
 
 
-def per_dispatch(d: str, counter: str) -> dict[str, list[float]]:
-    """Counter value (summed over the dimensions rocprofv3 reports) per dispatch, grouped by kernel."""
-    by_dispatch = collections.defaultdict(float)
+def per_dispatch(d: str, counter: str, reduce: str = "sum") -> dict[str, list[float]]:
+    """Counter value per dispatch (summed, or the maximum, over the dimensions rocprofv3
+    reports), grouped by kernel."""
+    by_dispatch = {}
     name_of = {}
     with open(_csv(d, "counter_collection.csv")) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
             key = int(r["Dispatch_Id"])
-            by_dispatch[key] += float(r["Counter_Value"])
+            v = float(r["Counter_Value"])
+            if key not in by_dispatch:
+                by_dispatch[key] = v
+            else:
+                by_dispatch[key] = max(by_dispatch[key], v) if reduce == "max" else by_dispatch[key] + v
             name_of[key] = short_name(r["Kernel_Name"])
     out = collections.defaultdict(list)
     for key in sorted(by_dispatch):
@@ -116,6 +121,49 @@ def traffic(fetch_dir: str, write_dir: str, calib_mib: int) -> dict:
             "kernels": kernels}
 
 
+SIMD_NUM = 1024  # 256 CUs x 4 SIMDs
+XCD_NUM = 8      # rocprofv3's GRBM_GUI_ACTIVE here is the sum over the 8 XCDs' GRBM blocks
+
+
+def dispatch_durations(d: str) -> dict[str, list[float]]:
+    """Kernel duration (s) per dispatch of a counter-collection run, from its own timestamps."""
+    dur, name_of = {}, {}
+    with open(_csv(d, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            name_of[key] = short_name(r["Kernel_Name"])
+    out = collections.defaultdict(list)
+    for key in sorted(dur):
+        out[name_of[key]].append(dur[key])
+    return out
+
+
+def mfma_summary(d: str) -> list[dict]:
+    """Per kernel: MFMA busy share of the SIMDs (SQ_VALU_MFMA_BUSY_CYCLES over the per-XCD
+    GRBM_GUI_ACTIVE x SIMDs, as rocprofv3's MfmaUtil), executed bf16 MFMA flops
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), vector instructions, and the core clock (per-XCD
+    GRBM_GUI_ACTIVE over the dispatch's duration)."""
+    busy = per_dispatch(d, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = per_dispatch(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    valu = per_dispatch(d, "SQ_INSTS_VALU")
+    gui = per_dispatch(d, "GRBM_GUI_ACTIVE")
+    dur = dispatch_durations(d)
+    mean = lambda v: sum(v) / len(v) if v else 0.0
+    rows = []
+    for name in sorted(busy):
+        if not name.startswith(("score_", "specpc_", "decode_")) or name not in gui:
+            continue
+        g = mean(gui[name]) / XCD_NUM
+        rows.append({"kernel": name, "dispatches": len(busy[name]),
+                     "mfma_busy_pct": round(100.0 * mean(busy[name]) / (g * SIMD_NUM), 1),
+                     "bf16_mfma_tflop": round(mean(mops.get(name, [])) * 512 / 1e12, 3),
+                     "valu_insts": round(mean(valu.get(name, []))),
+                     "ms": round(mean(dur[name]) * 1e3, 3),
+                     "clock_ghz": round(g / mean(dur[name]) / 1e9, 2)})
+    return rows
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--stats")
@@ -126,9 +174,20 @@ def main(argv=None):
     p.add_argument("--title", default="")
     p.add_argument("--command", action="append", default=[])
     p.add_argument("--bench-log", help="log of the profiled bench.py run: its JSON line's event timings are listed")
+    p.add_argument("--mfma", help="directory of a --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                                  "SQ_INSTS_VALU GRBM_GUI_ACTIVE run")
     p.add_argument("--out")
     a = p.parse_args(argv)
-    if a.stats:
+    if a.mfma:
+        lines = [f"# {a.title}" if a.title else "# MFMA and vector counters per kernel", ""]
+        lines += ["Command:", ""] + [f"    {c}" for c in a.command] + [""]
+        lines.append(f"{'kernel':<40} {'calls':>5} {'ms':>8} {'MFMA busy %':>11} {'bf16 TFLOP':>10} {'VALU insts':>12} "
+                     f"{'clock GHz':>9}")
+        for r in mfma_summary(a.mfma):
+            lines.append(f"{r['kernel'][:40]:<40} {r['dispatches']:>5} {r['ms']:>8} {r['mfma_busy_pct']:>11} "
+                         f"{r['bf16_mfma_tflop']:>10} {r['valu_insts']:>12} {r['clock_ghz']:>9}")
+        text = "\n".join(lines) + "\n"
+    elif a.stats:
         lines = [f"# {a.title}" if a.title else "# rocprofv3 kernel statistics", ""]
         lines += ["Command:", ""] + [f"    {c}" for c in a.command] + [""]
         lines.append(f"{'kernel':<44} {'calls':>6} {'total ms':>10} {'avg us':>10} {'%':>6}")
@@ -152,7 +211,7 @@ def main(argv=None):
         t.update({"workload": a.workload, "kernel_source_hash": kernel_source_hash(), "commands": a.command})
         text = json.dumps(t, indent=1) + "\n"
     else:
-        p.error("give --stats DIR, or --fetch DIR --write DIR")
+        p.error("give --stats DIR, --mfma DIR, or --fetch DIR --write DIR")
     if a.out:
         with open(a.out, "w") as f:
             f.write(text)

@@ -59,19 +59,15 @@ static int pc_maps_per_stage(int group) {
 // units; per unit its waves hold their keys as MFMA operands and the G query
 // heads' rows stream through LDS, several maps per barrier, the next stage's
 // rows loading while the current one is computed.
+// The block of key block kblk and row block rb; MASKED blocks hold keys past
+// the first window position (the causal diagonal).
 template <typename T, int D, bool MASKED>
-__global__ __launch_bounds__(SKV_PC_WAVES * 64, 1) void specpc_pass2_kernel(SpecPCArgs pa, int kblock0, int n_kblocks_launch) {
+__device__ __forceinline__ void specpc_pass2_block(const SpecPCArgs& pa, int rb, int kblk, char* smem) {
   using Gm = PcGeom<T, D>;
   const ScoreArgs& a = pa.sc;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mps = pa.maps_per_stage;
   char* s_rows = smem;                                                          // [2][mps][kMapBytes]
   float* s_lam = reinterpret_cast<float*>(smem + (size_t)2 * mps * Gm::kMapBytes);  // [2][mps][64]
-
-  // This launch covers key blocks [kblock0, kblock0 + n_kblocks_launch) of every row block.
-  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
-  // The row blocks of one key block are neighbours (same XCD, same time): the keys come from L2 after the first.
-  const int rb = logical % pa.n_rowblocks, kblk = kblock0 + logical / pa.n_rowblocks;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, half = lane / 32;
   const int W = a.rows_per_qhead, G = a.group;
   const int row0 = rb * Gm::kRowsPerBlock;                    // first window row of the block
@@ -222,6 +218,20 @@ __global__ __launch_bounds__(SKV_PC_WAVES * 64, 1) void specpc_pass2_kernel(Spec
   }
 }
 
+// One launch covers every (key block, row block): blocks whose keys all
+// precede the first window position (kblk < n_plain) need no causal mask.
+// Every block walks all (layer, query head) maps, so plain and masked
+// blocks take about the same time and share the rounds of the launch.
+template <typename T, int D>
+__global__ __launch_bounds__(SKV_PC_WAVES * 64, 1) void specpc_pass2_kernel(SpecPCArgs pa, int n_plain) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int logical = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  // The row blocks of one key block are neighbours (same XCD, same time): the keys come from L2 after the first.
+  const int rb = logical % pa.n_rowblocks, kblk = logical / pa.n_rowblocks;
+  if (kblk < n_plain) specpc_pass2_block<T, D, false>(pa, rb, kblk, smem);  // block-uniform
+  else specpc_pass2_block<T, D, true>(pa, rb, kblk, smem);
+}
+
 __global__ __launch_bounds__(256) void specpc_reduce_kernel(SpecPCArgs pa) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= pa.sc.n_keys) return;
@@ -248,21 +258,11 @@ static hipError_t launch_pc2(const SpecPCArgs& args, hipStream_t s) {
   int64_t n_plain = (a.sc.pos_base + 1) / Gm::kKeysPerBlock;
   if (n_plain > n_kblocks) n_plain = n_kblocks;
   if ((int64_t)n_kblocks * Gm::kKeysPerBlock > a.sc.n_keys && n_plain == n_kblocks) n_plain = n_kblocks - 1;
-  const int n_masked = n_kblocks - (int)n_plain;
-  if (n_plain > 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(specpc_pass2_kernel<T, D, false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    specpc_pass2_kernel<T, D, false><<<dim3((unsigned)(n_plain * a.n_rowblocks)), dim3(Gm::kThreads), lds, s>>>(
-        a, 0, (int)n_plain);
-  }
-  if (n_masked > 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(specpc_pass2_kernel<T, D, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    specpc_pass2_kernel<T, D, true><<<dim3((unsigned)(n_masked * a.n_rowblocks)), dim3(Gm::kThreads), lds, s>>>(
-        a, (int)n_plain, n_masked);
-  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(specpc_pass2_kernel<T, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  specpc_pass2_kernel<T, D><<<dim3((unsigned)(n_kblocks * a.n_rowblocks)), dim3(Gm::kThreads), lds, s>>>(
+      a, (int)n_plain);
   return hipGetLastError();
 }
 
