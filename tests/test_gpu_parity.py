@@ -67,6 +67,13 @@ def test_tiny_fp32_2k_full():
     _full_check(wl.TINY_FP32_2K, seed=1)
 
 
+def test_fp32_d64_group_16():
+    # fp32 at head_dim 64 with 16 query heads per KV head (1024 rows)
+    cfg = wl.reduced(wl.TINY_FP32_2K, n_layers=2, n_q_heads=16, n_kv_heads=1, n_in=1300, n_window=24, n_lookahead=40,
+                     C_max=100)
+    _full_check(cfg, seed=43)
+
+
 @pytest.mark.parametrize("pooled_out", [False, True])
 def test_empty_prefix_keeps_the_window(pooled_out):
     # n_window = n_in: nothing is scored (scores and pooled have no elements), the kept list is the
@@ -101,8 +108,12 @@ def test_empty_prefix_keeps_the_window(pooled_out):
     dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_in=300, n_window=20, n_lookahead=3, C_max=0),
     dict(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_in=33, n_window=32, n_lookahead=4, C_max=8),
     dict(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=128, n_in=37, n_window=32, n_lookahead=4, C_max=2),
+    dict(n_layers=3, n_q_heads=2, n_kv_heads=2, head_dim=128, n_in=900, n_window=1, n_lookahead=0, C_max=40),
+    dict(n_layers=1, n_q_heads=16, n_kv_heads=2, head_dim=128, n_in=1500, n_window=100, n_lookahead=500, C_max=64),
+    dict(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, n_in=3, n_window=1, n_lookahead=2, C_max=1),
 ], ids=["ragged-bf16-d128", "gqa7-d64", "window-only", "mha-cmax-npre", "cmax-above-npre", "cmax-zero",
-        "one-key-prefix", "prefix-shorter-than-pool"])
+        "one-key-prefix", "prefix-shorter-than-pool", "one-observation-row", "4800-rows-many-parts",
+        "two-key-prefix"])
 def test_small_bf16_shapes(case):
     cfg = wl.reduced(wl.LLAMA8B_16K, **case)
     _full_check(cfg, seed=11)
