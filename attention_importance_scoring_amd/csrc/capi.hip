@@ -327,6 +327,7 @@ skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_
   a.n_top = (int32_t)n_top;
   a.pool = pool;
   a.pool_radius = pool == SKV_POOL_NONE ? 0 : pool_kernel / 2;
+  a.write_pooled = pooled != nullptr;
   ProfScope p("select", s);
   return hip_status(launch_select(a, s));
 }

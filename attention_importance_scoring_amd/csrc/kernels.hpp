@@ -76,6 +76,7 @@ struct SelectArgs {
   int32_t n_top;            // min(C_max, n_pre)
   int32_t pool;             // skv_pool
   int32_t pool_radius;      // pool_kernel / 2
+  int32_t write_pooled;     // 0: `pooled` is workspace that only the run-time pool path needs
   // Two-stage form for long units with few heads: n_seg segments of seg_len
   // keys each keep their local top n_top as (key, index) candidates in
   // [n_units][n_seg][n_top] (workspace); a second kernel selects among them.

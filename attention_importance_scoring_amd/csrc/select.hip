@@ -7,10 +7,14 @@
 // order-preserving uint32 image of the fp32 pooled values.  For n_pre up to
 // 64K the keys stay in registers: wave w owns a contiguous index span, lane l
 // step i holds index w S + 64 i + l.
-//   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r;
+//   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r; the
+//      width-7 max pool (and no pooling) is computed in registers from one
+//      coalesced load per score, with lane rotations for the neighbours;
 //   2. the n_top-th largest key T is found bit by bit from the top
 //      (T | bit is kept when at least n_top keys are >= it), each count a
-//      per-lane sum, seven ballots and one sum over the 16 waves;
+//      per-lane sum, seven ballots and one sum over the 16 waves; the search
+//      ends early once the top set is known exactly or T's remaining range
+//      holds it as its largest key;
 //   3. keys > T are all taken, and of the keys equal to T the lowest-index
 //      k_rem ones; wave-level counts and scans over the waves give each wave
 //      its output offset, so one in-order sweep writes the kept list
@@ -134,16 +138,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 // Max pooling reads clamped neighbours: a truncated window only repeats
 // in-range values, which leaves the max unchanged, and the loads carry no
 // branches.
-template <int R>  // compile-time max-pool radius, or -1 for a run-time one
 __device__ __forceinline__ float pooled_at(const float* sc, int j, int n, int pool, int r) {
   if (pool == 1) {
     float v = sc[j];
-    if constexpr (R >= 0) {
-#pragma unroll
-      for (int o = 1; o <= R; ++o) v = fmaxf(v, fmaxf(sc[max(j - o, 0)], sc[min(j + o, n - 1)]));
-    } else {
-      for (int o = 1; o <= r; ++o) v = fmaxf(v, fmaxf(sc[max(j - o, 0)], sc[min(j + o, n - 1)]));
-    }
+    for (int o = 1; o <= r; ++o) v = fmaxf(v, fmaxf(sc[max(j - o, 0)], sc[min(j + o, n - 1)]));
     return v;
   }
   if (pool == 2 && r > 0) {
@@ -153,6 +151,50 @@ __device__ __forceinline__ float pooled_at(const float* sc, int j, int n, int po
     return s / (float)(hi - lo + 1);
   }
   return sc[j];
+}
+
+// Value held by lane (lane + o) mod 64.
+__device__ __forceinline__ float lane_rot(float v, int lane, int o) { return __shfl(v, (lane + o) & (kWave - 1)); }
+
+// Max pool of width 2R + 1 (R = 0 or 3) at the wave's positions
+// first + 64 i + lane, i < E, held in registers.  at(i) is the score at step
+// i's position, for i in [-1, E]: the caller clamps positions to [0, n), so
+// that a clamped neighbour repeats an in-range value, which leaves a max
+// unchanged (windows truncated at both ends), and a padding position next to
+// a valid one holds its real neighbour.  Each score is loaded once,
+// coalesced; the 7-wide window is the max of the four positions ending at p
+// and the four starting at p, built from maxima over pairs and fours with one
+// lane rotation each (the lanes a rotation wraps take the rotated value of
+// the adjacent step).
+template <int E, int R, class At>
+__device__ __forceinline__ void pool_regs(At at, int lane, float (&out)[E]) {
+  if constexpr (R == 0) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) out[i] = at(i);
+  } else {
+    static_assert(R == 3, "register pooling covers widths 1 and 7");
+    float x[E + 2];  // x[j]: step j - 1, j = 0 .. E + 1
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) x[j] = at(j - 1);
+    float rx[E + 2], m2[E + 2];  // m2[j] = max over positions p, p + 1
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) rx[j] = lane_rot(x[j], lane, 1);
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) {
+      const float nxt = rx[j + 1 < E + 2 ? j + 1 : j];  // the last step's lane 63 is never used
+      m2[j] = fmaxf(x[j], lane < kWave - 1 ? rx[j] : nxt);
+    }
+    float rm2[E + 2], m4[E + 1];  // m4[j] = max over positions p .. p + 3
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) rm2[j] = lane_rot(m2[j], lane, 2);
+#pragma unroll
+    for (int j = 0; j < E + 1; ++j) m4[j] = fmaxf(m2[j], lane < kWave - 2 ? rm2[j] : rm2[j + 1]);
+    float rm4[E + 1];  // rm4[j] = m4 three positions back (wrapped lanes fixed below)
+#pragma unroll
+    for (int j = 0; j < E + 1; ++j) rm4[j] = lane_rot(m4[j], lane, kWave - 3);
+#pragma unroll
+    for (int i = 0; i < E; ++i) out[i] = fmaxf(m4[i + 1], lane >= 3 ? rm4[i + 1] : rm4[i]);
+  }
 }
 
 // Sum of one value per wave over the block's 16 waves (every thread gets it).
@@ -176,6 +218,27 @@ __device__ __forceinline__ uint32_t waves_sum(uint32_t v, uint32_t* s_red, uint3
   return tot;
 }
 
+// Maximum over the wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Maximum of one wave-uniform value per wave over the block's 16 waves.
+__device__ __forceinline__ uint32_t waves_max(uint32_t v, uint32_t* s_red) {
+  if (threadIdx.x % kWave == 0) s_red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t m = 0u;
+#pragma unroll
+  for (int w4 = 0; w4 < kSelWaves / 4; ++w4) {
+    const u32x4 t4 = reinterpret_cast<const u32x4*>(s_red)[w4];
+    m = max(max(m, max(t4[0], t4[1])), max(t4[2], t4[3]));
+  }
+  __syncthreads();
+  return m;
+}
+
 // Sum over the wave of a per-lane count below 128, as seven ballots over
 // its bits (the result is wave-uniform).
 __device__ __forceinline__ uint32_t wave_count(uint32_t c) {
@@ -195,6 +258,8 @@ enum SelMode { kSelDirect = 0, kSelSegment = 1, kSelMerge = 2 };
 //            (so in index order); writes the kept list.
 // The unit's top n_top is contained in the union of the segments' own top
 // n_top (lowest indices first on ties in both), so the merge is exact.
+// R: 0 or 3 pools in registers (no pooling, or the width-7 max pool);
+// -1 takes the run-time pool mode and radius through the pooled buffer.
 template <int E, int R, int MODE>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_red[kSelWaves];
@@ -235,11 +300,33 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
       const uint32_t k = cand_key[pc];
       key[i] = (i * kWave < lim && pc - seg * a.n_top < seg_keep) ? k : 0u;
     }
+  } else if constexpr (R >= 0) {  // max pool of width 2R + 1 in registers
+    // Chunks of at most 32 steps, each with its own neighbour loads, bound
+    // the registers in flight next to the keys already made.
+    constexpr int C = E < 32 ? E : 32;
+#pragma unroll
+    for (int c = 0; c < E; c += C) {
+      float v[C];
+      const int first = s0 + base + c * kWave;
+      if (first >= kWave && first + (C + 1) * kWave <= n) {  // every load in range (wave-uniform)
+        const float* p = sc + first + lane;
+        pool_regs<C, R>([&](int i) { return p[i * kWave]; }, lane, v);
+      } else {
+        pool_regs<C, R>([&](int i) { return sc[min(max(first + i * kWave + lane, 0), n - 1)]; }, lane, v);
+      }
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const int st = c + i;
+        if (a.write_pooled && st * kWave < lim) pl[s0 + base + st * kWave + lane] = v[i];
+        key[st] = (st * kWave < lim) ? ordered_key(v[i]) : 0u;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
 #pragma unroll 8
     for (int i = 0; i < E; ++i) {
       const int p = base + i * kWave + lane;
-      if (i * kWave < lim) pl[s0 + p] = pooled_at<R>(sc, s0 + p, n, a.pool, a.pool_radius);
+      if (i * kWave < lim) pl[s0 + p] = pooled_at(sc, s0 + p, n, a.pool, a.pool_radius);
     }
     __syncthreads();  // the block's pooled values are visible to all its threads
     const float* pl_lane = pl + s0 + base + lane;
@@ -272,14 +359,45 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
     return;
   }
 
-  // 2. T = the n_top-th largest key
+  // 2. T = the n_top-th largest key, bit by bit from the top: T keeps the
+  //    bits found so far, at least n_top keys are >= T, fewer than n_top lie
+  //    above T's range [T, T + 2^(b+1)).  Two exits end the search early:
+  //    * exactly n_top keys are >= a candidate: they are the top n_top with
+  //      no tie across the boundary, and T = candidate - 1 takes nothing
+  //      equal to it (usual for distinct scores, about halfway down);
+  //    * after kPlateauBit, the largest key m in T's range: if at least n_top
+  //      keys are >= m, T is m (usual when max pooling has spread the
+  //      boundary value over neighbouring positions).
+  //    Half of each count goes through wave ballots (scalar popcounts), which
+  //    issue beside the vector compares of the other half.
+  constexpr int kPlateauBit = 15;
   uint32_t T = 0u, before;
   for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    uint32_t c = 0u;
+    if (b == kPlateauBit) {
+      uint32_t m = 0u;  // the range holds a key (at least n_top keys are >= T, fewer above the range)
 #pragma unroll
-    for (int i = 0; i < E; ++i) c += key[i] >= cand ? 1u : 0u;
-    if (waves_sum(wave_count(c), s_red, before) >= (uint32_t)n_top) T = cand;
+      for (int i = 0; i < E; ++i) m = (key[i] - T < (2u << b)) ? max(m, key[i]) : m;
+      m = waves_max(wave_max(m), s_red);
+      uint32_t c = 0u;
+#pragma unroll
+      for (int i = 0; i < E; ++i) c += key[i] >= m ? 1u : 0u;
+      if (waves_sum(wave_count(c), s_red, before) >= (uint32_t)n_top) {
+        T = m;
+        break;
+      }
+    }
+    const uint32_t cand = T | (1u << b);
+    uint32_t c = 0u, cs = 0u;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) c += key[i] >= cand ? 1u : 0u;
+#pragma unroll
+    for (int i = E / 2; i < E; ++i) cs += (uint32_t)__popcll(__ballot(key[i] >= cand));
+    const uint32_t cnt = waves_sum(wave_count(c) + cs, s_red, before);  // block-uniform
+    if (cnt == (uint32_t)n_top) {
+      T = cand - 1u;
+      break;
+    }
+    if (cnt > (uint32_t)n_top) T = cand;
   }
 
   // 3. ascending emission: every key > T, and the k_rem lowest-index keys == T
@@ -344,10 +462,12 @@ static void launch_mode(const SelectArgs& a, dim3 grid, int len, hipStream_t s) 
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const bool r3 = a.pool == 1 && a.pool_radius == 3;  // the width-7 max pool
+  const bool r3 = a.pool == 1 && a.pool_radius == 3;                       // the width-7 max pool
+  const bool r0 = a.pool_radius == 0;                                       // no pooling (or width 1)
   if (a.n_seg > 1) {
     const dim3 g1((unsigned)((int64_t)a.n_units * a.n_seg));
     if (r3) launch_mode<kSelSegment, 3>(a, g1, a.seg_len, s);
+    else if (r0) launch_mode<kSelSegment, 0>(a, g1, a.seg_len, s);
     else launch_mode<kSelSegment, -1>(a, g1, a.seg_len, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -356,6 +476,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   }
   if (per_lane(a.n_pre) <= kSelMaxPerLane) {
     if (r3) launch_mode<kSelDirect, 3>(a, dim3((unsigned)a.n_units), a.n_pre, s);
+    else if (r0) launch_mode<kSelDirect, 0>(a, dim3((unsigned)a.n_units), a.n_pre, s);
     else launch_mode<kSelDirect, -1>(a, dim3((unsigned)a.n_units), a.n_pre, s);
   } else {
     select_kernel<<<dim3((unsigned)a.n_units), dim3(kSelThreads), 0, s>>>(a);
