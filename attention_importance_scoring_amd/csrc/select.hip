@@ -7,9 +7,9 @@
 // order-preserving uint32 image of the fp32 pooled values.  For n_pre up to
 // 64K the keys stay in registers: wave w owns a contiguous index span, lane l
 // step i holds index w S + 64 i + l.
-//   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r; the
-//      width-7 max pool (and no pooling) is computed in registers from one
-//      coalesced load per score, with lane rotations for the neighbours;
+//   1. pooled[j] = max (or in-range mean) of scores over |j' - j| <= r; max
+//      pools up to width 65 (and no pooling) are computed in registers from
+//      one coalesced load per score, with lane rotations for the neighbours;
 //   2. the n_top-th largest key T is found bit by bit from the top
 //      (T | bit is kept when at least n_top keys are >= it), each count a
 //      per-lane sum, seven ballots and one sum over the 16 waves; the search
@@ -156,44 +156,81 @@ __device__ __forceinline__ float pooled_at(const float* sc, int j, int n, int po
 // Value held by lane (lane + o) mod 64.
 __device__ __forceinline__ float lane_rot(float v, int lane, int o) { return __shfl(v, (lane + o) & (kWave - 1)); }
 
-// Max pool of width 2R + 1 (R = 0 or 3) at the wave's positions
+// Max pool of width 2r + 1 (0 <= r <= 32) at the wave's positions
 // first + 64 i + lane, i < E, held in registers.  at(i) is the score at step
 // i's position, for i in [-1, E]: the caller clamps positions to [0, n), so
 // that a clamped neighbour repeats an in-range value, which leaves a max
 // unchanged (windows truncated at both ends), and a padding position next to
 // a valid one holds its real neighbour.  Each score is loaded once,
-// coalesced; the 7-wide window is the max of the four positions ending at p
-// and the four starting at p, built from maxima over pairs and fours with one
-// lane rotation each (the lanes a rotation wraps take the rotated value of
-// the adjacent step).
+// coalesced.  Maxima over the L positions starting at p are built by
+// doubling L; the window [p - r, p + r] is then the max of the L-window
+// starting at p - r and the one starting at p + r + 1 - L, for the largest
+// power of two L <= 2r + 1.  Every shift is one lane rotation: the lanes it
+// wraps take the rotated value of the adjacent step, and a wrapped lane of
+// the last step only reaches positions past the ones pooled.
+// R >= 0 fixes r at compile time; R = -2 takes r_rt.
 template <int E, int R, class At>
-__device__ __forceinline__ void pool_regs(At at, int lane, float (&out)[E]) {
-  if constexpr (R == 0) {
+__device__ __forceinline__ void pool_regs(At at, int lane, int r_rt, float (&out)[E]) {
+  const int r = R >= 0 ? R : r_rt;
+  float F[E + 2];  // F[j]: step j - 1, j = 0 .. E + 1
 #pragma unroll
-    for (int i = 0; i < E; ++i) out[i] = at(i);
-  } else {
-    static_assert(R == 3, "register pooling covers widths 1 and 7");
-    float x[E + 2];  // x[j]: step j - 1, j = 0 .. E + 1
+  for (int j = 0; j < E + 2; ++j) F[j] = at(j - 1);
+  if (r == 0) {
 #pragma unroll
-    for (int j = 0; j < E + 2; ++j) x[j] = at(j - 1);
-    float rx[E + 2], m2[E + 2];  // m2[j] = max over positions p, p + 1
+    for (int i = 0; i < E; ++i) out[i] = F[i + 1];
+    return;
+  }
+  if constexpr (R == 3) {
+    // Width 7: the max over pairs, then fours, then the four ending at p
+    // and the four starting at p (fewer live values than the general form).
+    float rx[E + 2], m2[E + 2];
 #pragma unroll
-    for (int j = 0; j < E + 2; ++j) rx[j] = lane_rot(x[j], lane, 1);
+    for (int j = 0; j < E + 2; ++j) rx[j] = lane_rot(F[j], lane, 1);
 #pragma unroll
     for (int j = 0; j < E + 2; ++j) {
       const float nxt = rx[j + 1 < E + 2 ? j + 1 : j];  // the last step's lane 63 is never used
-      m2[j] = fmaxf(x[j], lane < kWave - 1 ? rx[j] : nxt);
+      m2[j] = fmaxf(F[j], lane < kWave - 1 ? rx[j] : nxt);
     }
-    float rm2[E + 2], m4[E + 1];  // m4[j] = max over positions p .. p + 3
+    float rm2[E + 2], m4[E + 1];
 #pragma unroll
     for (int j = 0; j < E + 2; ++j) rm2[j] = lane_rot(m2[j], lane, 2);
 #pragma unroll
     for (int j = 0; j < E + 1; ++j) m4[j] = fmaxf(m2[j], lane < kWave - 2 ? rm2[j] : rm2[j + 1]);
-    float rm4[E + 1];  // rm4[j] = m4 three positions back (wrapped lanes fixed below)
+    float rm4[E + 1];
 #pragma unroll
     for (int j = 0; j < E + 1; ++j) rm4[j] = lane_rot(m4[j], lane, kWave - 3);
 #pragma unroll
     for (int i = 0; i < E; ++i) out[i] = fmaxf(m4[i + 1], lane >= 3 ? rm4[i + 1] : rm4[i]);
+    return;
+  }
+  int L = 1;
+  for (; 2 * L <= 2 * r + 1; L *= 2) {  // F: max over [p, p + L) -> over [p, p + 2L)
+    float nxt = lane_rot(F[0], lane, L);
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) {
+      const float cur = nxt;
+      if (j + 1 < E + 2) nxt = lane_rot(F[j + 1], lane, L);
+      F[j] = fmaxf(F[j], lane + L < kWave ? cur : nxt);
+    }
+  }
+  const int s = r + 1 - L;  // second window's start relative to p, in (-r, L)
+  float RA[E + 1], RS[E + 2];
+#pragma unroll
+  for (int j = 0; j < E + 1; ++j) RA[j] = lane_rot(F[j], lane, kWave - r);
+  if (s == 0) {
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) RS[j] = F[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < E + 2; ++j) RS[j] = lane_rot(F[j], lane, s);
+  }
+  const bool a_here = lane >= r, b_here = (unsigned)(lane + s) < (unsigned)kWave;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int j = i + 1;
+    const float a = a_here ? RA[j] : RA[j - 1];                               // window at p - r
+    const float b = b_here ? RS[j] : (s >= 0 ? RS[j + 1] : RS[j - 1]);        // window at p + s
+    out[i] = fmaxf(a, b);
   }
 }
 
@@ -258,8 +295,9 @@ enum SelMode { kSelDirect = 0, kSelSegment = 1, kSelMerge = 2 };
 //            (so in index order); writes the kept list.
 // The unit's top n_top is contained in the union of the segments' own top
 // n_top (lowest indices first on ties in both), so the merge is exact.
-// R: 0 or 3 pools in registers (no pooling, or the width-7 max pool);
-// -1 takes the run-time pool mode and radius through the pooled buffer.
+// R: 0 or 3 pools in registers with that radius (no pooling, the width-7 max
+// pool), -2 the max pool of the run-time radius (at most 32) in registers,
+// -1 any pool mode and radius through the pooled buffer.
 template <int E, int R, int MODE>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_red[kSelWaves];
@@ -300,19 +338,20 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
       const uint32_t k = cand_key[pc];
       key[i] = (i * kWave < lim && pc - seg * a.n_top < seg_keep) ? k : 0u;
     }
-  } else if constexpr (R >= 0) {  // max pool of width 2R + 1 in registers
-    // Chunks of at most 32 steps, each with its own neighbour loads, bound
-    // the registers in flight next to the keys already made.
-    constexpr int C = E < 32 ? E : 32;
+  } else if constexpr (R != -1) {  // max pool in registers
+    // Chunks of steps, each with its own neighbour loads, bound the registers
+    // in flight next to the keys already made.
+    constexpr int C = E <= 32 ? E : (R >= 0 ? 32 : (MODE == kSelDirect ? 16 : 8));
 #pragma unroll
     for (int c = 0; c < E; c += C) {
       float v[C];
       const int first = s0 + base + c * kWave;
       if (first >= kWave && first + (C + 1) * kWave <= n) {  // every load in range (wave-uniform)
         const float* p = sc + first + lane;
-        pool_regs<C, R>([&](int i) { return p[i * kWave]; }, lane, v);
+        pool_regs<C, R>([&](int i) { return p[i * kWave]; }, lane, a.pool_radius, v);
       } else {
-        pool_regs<C, R>([&](int i) { return sc[min(max(first + i * kWave + lane, 0), n - 1)]; }, lane, v);
+        pool_regs<C, R>([&](int i) { return sc[min(max(first + i * kWave + lane, 0), n - 1)]; }, lane,
+                        a.pool_radius, v);
       }
 #pragma unroll
       for (int i = 0; i < C; ++i) {
@@ -429,6 +468,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
 }
 
 constexpr int kSelMaxPerLane = 64;
+constexpr int kRegPoolMaxRadius = 32;  // register pools reach one step (64 positions) to either side
 
 static int per_lane(int64_t len) { return (int)((len + kSelThreads - 1) / kSelThreads); }
 
@@ -458,16 +498,20 @@ static void launch_mode(const SelectArgs& a, dim3 grid, int len, hipStream_t s) 
   else if (e <= 8) select_reg_kernel<8, R, MODE><<<grid, block, 0, s>>>(a);
   else if (e <= 16) select_reg_kernel<16, R, MODE><<<grid, block, 0, s>>>(a);
   else if (e <= 32) select_reg_kernel<32, R, MODE><<<grid, block, 0, s>>>(a);
+  else if constexpr (R == -2 && MODE == kSelSegment)  // the register pool of a run-time radius
+    select_reg_kernel<64, -1, MODE><<<grid, block, 0, s>>>(a);  // would not fit beside 64 segment keys
   else select_reg_kernel<64, R, MODE><<<grid, block, 0, s>>>(a);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const bool r3 = a.pool == 1 && a.pool_radius == 3;                       // the width-7 max pool
   const bool r0 = a.pool_radius == 0;                                       // no pooling (or width 1)
+  const bool rmax = a.pool == 1 && a.pool_radius <= kRegPoolMaxRadius;      // other max pools in registers
   if (a.n_seg > 1) {
     const dim3 g1((unsigned)((int64_t)a.n_units * a.n_seg));
     if (r3) launch_mode<kSelSegment, 3>(a, g1, a.seg_len, s);
     else if (r0) launch_mode<kSelSegment, 0>(a, g1, a.seg_len, s);
+    else if (rmax) launch_mode<kSelSegment, -2>(a, g1, a.seg_len, s);
     else launch_mode<kSelSegment, -1>(a, g1, a.seg_len, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -477,6 +521,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (per_lane(a.n_pre) <= kSelMaxPerLane) {
     if (r3) launch_mode<kSelDirect, 3>(a, dim3((unsigned)a.n_units), a.n_pre, s);
     else if (r0) launch_mode<kSelDirect, 0>(a, dim3((unsigned)a.n_units), a.n_pre, s);
+    else if (rmax) launch_mode<kSelDirect, -2>(a, dim3((unsigned)a.n_units), a.n_pre, s);
     else launch_mode<kSelDirect, -1>(a, dim3((unsigned)a.n_units), a.n_pre, s);
   } else {
     select_kernel<<<dim3((unsigned)a.n_units), dim3(kSelThreads), 0, s>>>(a);

@@ -11,8 +11,8 @@ against the oracle's rule applied to the GPU's own pooled values.
 
 The cases reach every selection form: one block per unit with the keys in
 registers (unit counts of 128 and more), two stages over segments (fewer
-units), the single-block radix select beyond 64K keys per block, the width-7
-and width-1 pools in registers and other widths through the pooled buffer, and
+units), the single-block radix select beyond 64K keys per block, max pools of
+widths up to 65 in registers and other pools through the pooled buffer, and
 score sets whose cut-off is tied (plateaus from max pooling, rounded values,
 constants), distinct, signed, or tiny."""
 import numpy as np
@@ -82,9 +82,22 @@ def test_registers_64k_keys_per_block(kind):
     _run(128, 65504, 32, 256, "max", 7, kind)
 
 
-@pytest.mark.parametrize("pool,k", [("max", 7), ("none", 1), ("max", 1), ("max", 9), ("avg", 5)])
+@pytest.mark.parametrize("pool,k", [("max", 7), ("none", 1), ("max", 1), ("max", 9), ("avg", 5), ("avg", 1)])
 def test_pool_forms(pool, k):
     _run(130, 20000, 16, 300, pool, k, "heavy", seed=3)
+
+
+@pytest.mark.parametrize("k", [3, 5, 13, 15, 33, 43, 63, 65, 67])
+def test_max_pool_widths(k):
+    # widths up to 65 pool in registers (doubling windows), 67 through the pooled buffer;
+    # 64 keys per lane (direct) and a few per lane (two stages)
+    _run(128, 65504, 8, 256, "max", k, "heavy", seed=k)
+    _run(2, 30000, 3, 700, "max", k, "plateaus", seed=k + 1)
+
+
+def test_two_stage_long_segments_other_width():
+    # segments of 33334 keys (64 per lane) with a width-15 max pool
+    _run(2, 200000, 0, 6000, "max", 15, "heavy", seed=13)
 
 
 @pytest.mark.parametrize("C_max", [1, 2, 99, 100, 150])
