@@ -82,6 +82,40 @@ ScoreWs score_ws(const Dims& d, int64_t units, int64_t rows, int64_t keys) {
   return w;
 }
 
+// SpecKV scoring runs pass 1 over the rows of a whole GQA group per KV head
+// in both selection granularities: every row's normaliser is the same, and
+// the per-query-head row order ([query head][row] per KV head) is the
+// grouped order, so the row statistics land where a per-query-head pass 2
+// reads them, while each K row is read once per pass-1 block instead of once
+// per query head.  Pass 2 runs one unit per SpecKV head (KV or query head):
+// the query heads of one KV head are neighbouring blocks and share its keys
+// through L2.
+struct SpecKVPlans {
+  int64_t units1, rows1, units2, rows2;
+  ScorePlan pl1, pl2;
+  ScoreWs ws;
+};
+SpecKVPlans speckv_plans(const Dims& d, int64_t n_pre) {
+  const int64_t n_obs = d.n_window + d.n_lookahead;
+  SpecKVPlans p;
+  p.units1 = d.L * d.Hkv;
+  p.rows1 = (d.Hq / d.Hkv) * n_obs;
+  p.units2 = d.L * d.heads();
+  p.rows2 = d.group() * n_obs;
+  p.pl1 = ScorePlan{1, 1, 32, 1, 2, 0, 0};
+  p.pl2 = p.pl1;
+  if (n_pre > 0 && n_obs > 0) {
+    score_plan(d.dtype, (int)d.D, p.units1, p.rows1, n_pre, &p.pl1);
+    score_plan(d.dtype, (int)d.D, p.units2, p.rows2, n_pre, &p.pl2);
+  }
+  const int64_t partials = p.pl2.n_parts - 1;
+  p.ws.part = 0;
+  p.ws.lam = round_up((size_t)(p.units1 * p.pl1.n_chunks * p.rows1) * sizeof(float2));
+  p.ws.colpart = p.ws.lam + round_up((size_t)(p.units1 * p.rows1) * sizeof(float));
+  p.ws.end = p.ws.colpart + round_up((size_t)(partials * p.units2 * n_pre) * sizeof(float));
+  return p;
+}
+
 struct PcWs {
   ScoreWs sc;
   size_t rowmax, end;
@@ -221,9 +255,9 @@ skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t*
   SKV_TRY(check_shape(shape, &d));
   if (!out) return SKV_ERR_NULL;
   if (C_max < 0) return SKV_ERR_PARAM;
-  const int64_t units = d.L * d.heads(), G = d.group();
+  const int64_t units = d.L * d.heads();
   const int64_t n_pre = d.n_in - d.n_window;
-  size_t need = score_ws(d, units, G * (d.n_window + d.n_lookahead), n_pre).end;           // speckv_scores
+  size_t need = speckv_plans(d, n_pre).ws.end;                                               // speckv_scores
   need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)) +                   // speckv_select
                             select_candidate_bytes(units, n_pre, keep_count(d, C_max) - d.n_window));
   need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
@@ -239,10 +273,10 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
   if (!q_obs || !k || (!scores && n_pre > 0)) return SKV_ERR_NULL;  // an empty prefix has no scores
   if (n_obs < 1) return SKV_ERR_SHAPE;
-  if (d.group() * n_obs > kMaxRows) return SKV_ERR_SHAPE;
+  if ((d.Hq / d.Hkv) * n_obs > kMaxRows) return SKV_ERR_SHAPE;
   if (!aligned(q_obs, 16) || !aligned(k, 16) || !aligned(scores, 4)) return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.heads(), G = d.group();
-  const ScoreWs w = score_ws(d, units, G * n_obs, n_pre);
+  const SpecKVPlans pp = speckv_plans(d, n_pre);
+  const ScoreWs& w = pp.ws;
   if (n_pre == 0) return SKV_OK;
   if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
@@ -255,17 +289,9 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.k_head_stride = d.stride;
   a.k_layer_stride = d.Hkv * d.stride;
   a.layer0 = 0;
-  a.n_units = (int32_t)units;
-  a.n_kv_heads = (int32_t)d.heads();
-  a.kv_repeat = (int32_t)d.repeat();
   a.agg_max = d.agg == SKV_AGG_MAX;
-  a.group = (int32_t)G;
   a.rows_per_qhead = (int32_t)n_obs;
-  a.n_rows = (int32_t)(G * n_obs);
   a.n_keys = (int32_t)n_pre;
-  ScorePlan pl;
-  score_plan(d.dtype, (int)d.D, units, G * n_obs, n_pre, &pl);
-  apply_plan(a, pl);
   a.causal = 0;
   a.pos_base = 0;
   a.c = d.scale * 1.4426950408889634f;
@@ -274,14 +300,28 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.lam = reinterpret_cast<float*>(base + w.lam);
   a.colpart = reinterpret_cast<float*>(base + w.colpart);
   a.scores = scores;
-  SKV_TRY(run_scoring(d, a, pl, s));
+  ScoreArgs a1 = a;  // pass 1: one unit per (layer, KV head), the whole group's rows
+  a1.n_units = (int32_t)pp.units1;
+  a1.n_kv_heads = (int32_t)d.Hkv;
+  a1.kv_repeat = 1;
+  a1.group = (int32_t)(d.Hq / d.Hkv);
+  a1.n_rows = (int32_t)pp.rows1;
+  apply_plan(a1, pp.pl1);
+  SKV_TRY(run_scoring(d, a1, pp.pl1, s));
+  ScoreArgs a2 = a;  // pass 2: one unit per SpecKV head
+  a2.n_units = (int32_t)pp.units2;
+  a2.n_kv_heads = (int32_t)d.heads();
+  a2.kv_repeat = (int32_t)d.repeat();
+  a2.group = (int32_t)d.group();
+  a2.n_rows = (int32_t)pp.rows2;
+  apply_plan(a2, pp.pl2);
   {
     ProfScope p("score_pass2", s);
-    SKV_TRY(hip_status(launch_score_pass2(d.dtype, (int)d.D, pl.kt, a, pl.lds_pass2, s)));
+    SKV_TRY(hip_status(launch_score_pass2(d.dtype, (int)d.D, pp.pl2.kt, a2, pp.pl2.lds_pass2, s)));
   }
-  if (a.n_parts == 1) return SKV_OK;
+  if (a2.n_parts == 1) return SKV_OK;
   ProfScope p("colsum_combine", s);
-  return hip_status(launch_colsum_combine(a, s));
+  return hip_status(launch_colsum_combine(a2, s));
 }
 
 skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,

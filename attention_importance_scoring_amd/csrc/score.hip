@@ -435,13 +435,12 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
     load_keys<T, D, KT>(a, unit, wave_kbase(0), kst);
     float colsum[Gm::kKT];
+#pragma unroll
+    for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
+    int in_sum = 0;  // tiles of the current sub-chunk done
     for (int it = 0; it < n_iter; ++it) {
       const IterPos cu = iter_pos(it, n_tiles, rot);
-      if (cu.j == 0) {  // new sub-chunk
-        if (cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);
-#pragma unroll
-        for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
-      }
+      if (cu.j == 0 && cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);  // new sub-chunk
       float lam[16];
       read_lam(cu.rt, lam);
       f32x16 acc[Gm::kKT];
@@ -458,14 +457,16 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         for (int i = 4; i < 16; ++i) s4[i & 3] = agg2<MAX>(s4[i & 3], fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i])));
         colsum[kt] = agg2<MAX>(colsum[kt], agg2<MAX>(agg2<MAX>(s4[0], s4[1]), agg2<MAX>(s4[2], s4[3])));
       }
-      if (cu.j + 1 == n_tiles) {  // sub-chunk complete for this part
+      if (++in_sum == n_tiles) {  // sub-chunk complete for this part: write, then restart the sums
         const int kbase = wave_kbase(cu.sc);
 #pragma unroll
         for (int kt = 0; kt < Gm::kKT; ++kt) {
           const float tot = agg2<MAX>(colsum[kt], shfl_xor32(colsum[kt]));
           const int key = kbase + kt * 32 + lane;
           if (lane < 32 && key < a.n_keys) out[key] = tot;
+          colsum[kt] = 0.f;
         }
+        in_sum = 0;
       }
     }
   }

@@ -193,14 +193,23 @@ def test_logit_jumps_between_key_groups(late):
     np.testing.assert_allclose(got.sum(-1), cfg.G * cfg.n_obs, rtol=1e-4)
 
 
+# Shapes: (n_window, n_lookahead, Hq, Hkv).  With one kept set per query head,
+# pass 2 keeps per-head column sums over the grouped rows when n_obs is a
+# multiple of 32 and a head fits a block (96: one part of 4 heads; 160: parts
+# of 3 and 2 heads), and runs one unit per query head otherwise (130; 640
+# rows per head exceed a block).
+_VARIANT_SHAPES = {"obs130": (40, 90, 8, 2), "obs96": (32, 64, 8, 2), "obs160": (32, 128, 10, 2),
+                   "obs640": (64, 576, 4, 2)}
+
+
+@pytest.mark.parametrize("shape_id", list(_VARIANT_SHAPES))
 @pytest.mark.parametrize("agg,pqh", [("max", False), ("sum", True), ("max", True)],
                          ids=["max-per-kv-head", "sum-per-query-head", "max-per-query-head"])
-def test_aggregation_and_per_query_head_variants(agg, pqh):
-    # G * n_obs = 520 rows: two row parts per KV head, so the max aggregation
-    # also crosses the part combine.
-    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=3000, n_window=40, n_lookahead=90,
-                     C_max=150)
-    print(f"\n[case] aggregation {agg}, per_query_head {pqh}", flush=True)
+def test_aggregation_and_per_query_head_variants(agg, pqh, shape_id):
+    n_window, n_lookahead, Hq, Hkv = _VARIANT_SHAPES[shape_id]
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_q_heads=Hq, n_kv_heads=Hkv, n_in=3000, n_window=n_window,
+                     n_lookahead=n_lookahead, C_max=150)
+    print(f"\n[case] aggregation {agg}, per_query_head {pqh}, {shape_id}", flush=True)
     host = wl.speckv_inputs(cfg, 17, "cpu")
     inp = _to(host, "cuda")
     L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
