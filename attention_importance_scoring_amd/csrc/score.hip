@@ -273,7 +273,10 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
   {
     const int row0 = bp.part * a.rows_per_part;
     const int prow = min(a.rows_per_part, a.n_rows - row0);
-    const int n_tiles = (prow + 31) / 32;
+    // Every part walks the same number of row tiles (a shorter last part
+    // pads with zero rows, whose statistics are never written), so the parts
+    // of a chunk read each key group at the same pace and share it in L2.
+    const int n_tiles = a.rows_per_part / 32;
     const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
     const int n_iter = n_sub * n_tiles;
     stage_rows<T, D, KT>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
