@@ -357,17 +357,30 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreArgs a) {
 }
 
 // scores += column sums of parts 1 .. n_parts - 1, in part order (or their
-// maximum, for the max aggregation).
-__global__ __launch_bounds__(256) void colsum_combine_kernel(ScoreArgs a) {
+// maximum, for the max aggregation).  Four consecutive elements per thread:
+// 16-byte accesses when both buffers are 16-byte aligned, else one by one.
+__global__ __launch_bounds__(256) void colsum_combine_kernel(ScoreArgs a, int vec) {
   const int64_t n = (int64_t)a.n_units * a.n_keys;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
-  float v = a.scores[idx];
-  for (int p = 1; p < a.n_parts; ++p) {
-    const float x = a.colpart[(int64_t)(p - 1) * n + idx];
-    v = a.agg_max ? fmaxf(v, x) : v + x;
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  if (vec && i0 + 4 <= n) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(a.scores + i0);
+    for (int p = 1; p < a.n_parts; ++p) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a.colpart + (int64_t)(p - 1) * n + i0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a.agg_max ? fmaxf(v[e], x[e]) : v[e] + x[e];
+    }
+    *reinterpret_cast<f32x4*>(a.scores + i0) = v;
+    return;
   }
-  a.scores[idx] = v;
+  for (int64_t idx = i0; idx < i0 + 4 && idx < n; ++idx) {
+    float v = a.scores[idx];
+    for (int p = 1; p < a.n_parts; ++p) {
+      const float x = a.colpart[(int64_t)(p - 1) * n + idx];
+      v = a.agg_max ? fmaxf(v, x) : v + x;
+    }
+    a.scores[idx] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -586,7 +599,10 @@ hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s) {
 
 hipError_t launch_colsum_combine(const ScoreArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_units * a.n_keys;
-  colsum_combine_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
+  const int vec = (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.colpart) % 16 == 0) &&
+                  (n % 4 == 0);
+  const int64_t threads = (n + 3) / 4;
+  colsum_combine_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(a, vec);
   return hipGetLastError();
 }
 

@@ -238,6 +238,32 @@ def test_aggregation_and_per_query_head_variants(agg, pqh, shape_id):
     assert_compacted(kc, vc, inp["k"].repeat_interleave(rep, dim=1), inp["v"].repeat_interleave(rep, dim=1), kept)
 
 
+@pytest.mark.parametrize("agg", ["sum", "max"])
+def test_scores_buffer_at_4_byte_offset(agg):
+    # 520 rows per KV head: two row parts, so the part combine runs; a scores
+    # buffer only 4-byte aligned takes its element-by-element path and must
+    # give the same bits as the 16-byte path
+    cfg = wl.reduced(wl.LLAMA8B_16K, n_layers=2, n_q_heads=8, n_kv_heads=2, n_in=3001, n_window=40, n_lookahead=90,
+                     C_max=150)
+    print(f"\n[case] scores at a 4-byte offset, aggregation {agg}", flush=True)
+    inp = wl.speckv_inputs(cfg, 19, "cuda")
+    shape = skv.make_shape(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_in, cfg.n_window,
+                           cfg.n_lookahead, skv.SKV_BF16, kv_head_stride=inp["kv_head_stride"],
+                           aggregation=skv.SKV_AGG_MAX if agg == "max" else skv.SKV_AGG_SUM)
+    ws = workspace(shape, cfg.C_max)
+    n = cfg.n_layers * cfg.n_kv_heads * cfg.n_pre
+    aligned = torch.empty(n, dtype=torch.float32, device="cuda")
+    big = torch.empty(n + 1, dtype=torch.float32, device="cuda")
+    shifted = big[1:]
+    assert aligned.data_ptr() % 16 == 0 and shifted.data_ptr() % 16 == 4
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], aligned, ws)
+    skv.speckv_scores(shape, inp["q_obs"], inp["k_buf"], shifted, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned, shifted)
+    want = oracle.speckv_scores(np64(inp["q_obs"]), np64(inp["k"]), cfg.n_window, aggregation=agg)
+    assert_scores_close(aligned.view(cfg.n_layers, cfg.n_kv_heads, cfg.n_pre).cpu().numpy(), want, cfg.G, cfg.n_obs)
+
+
 def test_in_place_equals_out_of_place_and_deterministic():
     cfg = wl.reduced(wl.LLAMA8B_128K_INPLACE, n_layers=2, n_in=5000, n_window=64, n_lookahead=64, C_max=300)
     host = wl.speckv_inputs(cfg, 7, "cpu")
