@@ -95,6 +95,13 @@ def test_max_pool_widths(k):
     _run(2, 30000, 3, 700, "max", k, "plateaus", seed=k + 1)
 
 
+@pytest.mark.parametrize("n_pre", [100, 5000, 10000], ids=["e4", "e8", "e16"])
+@pytest.mark.parametrize("k", [5, 43])
+def test_max_pool_widths_fewer_keys_per_lane(n_pre, k):
+    # the register pool of a run-time radius at 1, 5 and 10 keys per lane (one block per unit)
+    _run(130, n_pre, 3, 64, "max", k, "heavy", seed=n_pre + k)
+
+
 def test_two_stage_long_segments_other_width():
     # segments of 33334 keys (64 per lane) with a width-15 max pool
     _run(2, 200000, 0, 6000, "max", 15, "heavy", seed=13)
