@@ -31,8 +31,11 @@
  *     exception crosses this interface.
  *   - NaN or Inf inputs give undefined (but memory-safe) results.
  *   - Element types: SKV_F32 (float) or SKV_BF16 (bfloat16 stored as
- *     uint16).  head_dim must be 64 or 128.  Device pointers must be 16-byte
- *     aligned, and kv_head_stride * element size must be a multiple of 16.
+ *     uint16).  head_dim must be 64 or 128.  Query, key and value buffers
+ *     (inputs and compacted or gathered outputs) and the workspace must be
+ *     16-byte aligned, and kv_head_stride * element size must be a multiple
+ *     of 16; score, pooled, weight, index and decode-output buffers need
+ *     4-byte alignment.  A violation returns SKV_ERR_ALIGN.
  */
 #ifndef SPECKV_H
 #define SPECKV_H
@@ -120,12 +123,14 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
 
 /* SpecKV selection ("Key designs", SpecKV; "Loss / training strategy",
  * local pooling).  Per head: pooled = pool1d(scores) over the n_pre prefix
- * scores (stride 1, odd pool_kernel, windows truncated at both ends; max or
- * in-range mean; SKV_POOL_NONE copies); then the min(C_max, n_pre) best
- * prefix keys, ordered by pooled score descending and lower index first on
- * ties, plus every window key n_pre .. n_in - 1; written ascending.
- * Inputs : scores float [n_layers][H][n_pre] (non-negative; NULL when
- *          n_pre = 0, where the kept list is the window alone).
+ * scores (stride 1, odd pool_kernel in 1 .. 4097, windows truncated at both
+ * ends; max or in-range mean; SKV_POOL_NONE copies); then the
+ * min(C_max, n_pre) best prefix keys, ordered by pooled score descending and
+ * lower index first on ties (-0 equals +0), plus every window key
+ * n_pre .. n_in - 1; written ascending.
+ * Inputs : scores float [n_layers][H][n_pre] (any finite values, non-negative
+ *          from speckv_scores; NULL when n_pre = 0, where the kept list is
+ *          the window alone).
  * Outputs: kept int32 [n_layers][H][n_keep]; pooled float
  *          [n_layers][H][n_pre] or NULL.
  * The SpecPC token selection is this call on a shape with n_layers = 1,
