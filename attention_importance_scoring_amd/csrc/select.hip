@@ -301,6 +301,7 @@ enum SelMode { kSelDirect = 0, kSelSegment = 1, kSelMerge = 2 };
 template <int E, int R, int MODE>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_red[kSelWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t s_cnt[2][kSelWaves];  // the threshold search's counts
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = a.n_pre;
   int unit = blockIdx.x, s0 = 0, len = n, n_top = a.n_top;
@@ -404,15 +405,19 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
   //    * exactly n_top keys are >= a candidate: they are the top n_top with
   //      no tie across the boundary, and T = candidate - 1 takes nothing
   //      equal to it (usual for distinct scores, about halfway down);
-  //    * after kPlateauBit, the largest key m in T's range: if at least n_top
-  //      keys are >= m, T is m (usual when max pooling has spread the
-  //      boundary value over neighbouring positions).
-  //    Half of each count goes through wave ballots (scalar popcounts), which
-  //    issue beside the vector compares of the other half.
-  constexpr int kPlateauBit = 15;
+  //    * after 16 and after 24 bits, the largest key m in T's range: if at
+  //      least n_top keys are >= m, T is m (usual when max pooling has spread
+  //      the boundary value over neighbouring positions).
+  //    Each count adds vector compares for 3/8 of the keys and wave ballots
+  //    with scalar popcounts for the rest (the two issue side by side), then
+  //    one sum over the waves through a double-buffered LDS row: one barrier
+  //    per bit (a wave writes a row only after every wave has passed the
+  //    barrier that followed its previous reads of that row).
+  constexpr int kVecCount = (3 * E) / 8;
   uint32_t T = 0u, before;
+  int round = 0;
   for (int b = 31; b >= 0; --b) {
-    if (b == kPlateauBit) {
+    if (b == 15 || b == 7) {
       uint32_t m = 0u;  // the range holds a key (at least n_top keys are >= T, fewer above the range)
 #pragma unroll
       for (int i = 0; i < E; ++i) m = (key[i] - T < (2u << b)) ? max(m, key[i]) : m;
@@ -428,10 +433,20 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(SelectArgs a) {
     const uint32_t cand = T | (1u << b);
     uint32_t c = 0u, cs = 0u;
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) c += key[i] >= cand ? 1u : 0u;
+    for (int i = 0; i < kVecCount; ++i) c += key[i] >= cand ? 1u : 0u;
 #pragma unroll
-    for (int i = E / 2; i < E; ++i) cs += (uint32_t)__popcll(__ballot(key[i] >= cand));
-    const uint32_t cnt = waves_sum(wave_count(c) + cs, s_red, before);  // block-uniform
+    for (int i = kVecCount; i < E; ++i) cs += (uint32_t)__popcll(__ballot(key[i] >= cand));
+    const uint32_t wc = wave_count(c) + cs;  // ballots: every lane active
+    uint32_t* row = s_cnt[round & 1];
+    ++round;
+    if (lane == 0) row[wave] = wc;
+    __syncthreads();
+    uint32_t cnt = 0u;  // block-uniform
+#pragma unroll
+    for (int w4 = 0; w4 < kSelWaves / 4; ++w4) {
+      const u32x4 t4 = reinterpret_cast<const u32x4*>(row)[w4];
+      cnt += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+    }
     if (cnt == (uint32_t)n_top) {
       T = cand - 1u;
       break;
