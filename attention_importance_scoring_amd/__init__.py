@@ -99,6 +99,20 @@ def specpc_gather_tokens(shape: Shape, k, v, tokens, n_tokens: int, k_out, v_out
            "specpc_gather_tokens")
 
 
+def speckv_scores_rows(shape: Shape, q_obs, k, rows, n_src_rows: int, scores, workspace, stream=None):
+    w, wb = _ws(workspace)
+    _check(_lib.load().speckv_scores_rows(ctypes.byref(shape), _ptr(q_obs, "q_obs"), _ptr(k, "k"), _ptr(rows, "rows"),
+                                          n_src_rows, _ptr(scores, "scores"), w, wb, _stream(stream)),
+           "speckv_scores_rows")
+
+
+def speckv_compact_rows(shape: Shape, k, v, rows, n_src_rows: int, kept, n_keep: int, k_out, v_out, stream=None):
+    _check(_lib.load().speckv_compact_rows(ctypes.byref(shape), _ptr(k, "k"), _ptr(v, "v"), _ptr(rows, "rows"),
+                                           n_src_rows, _ptr(kept, "kept"), n_keep, _ptr(k_out, "k_out"),
+                                           _ptr(v_out, "v_out"), _stream(stream)),
+           "speckv_compact_rows")
+
+
 def specpc_token_scores(shape: Shape, l_skip: int, q_win, k, query_weights, token_scores, workspace, stream=None):
     w, wb = _ws(workspace)
     _check(_lib.load().specpc_token_scores(ctypes.byref(shape), l_skip, _ptr(q_win, "q_win"), _ptr(k, "k"),

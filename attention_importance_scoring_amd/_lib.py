@@ -23,8 +23,9 @@ SKV_AGG_SUM, SKV_AGG_MAX = 0, 1
 # Every symbol include/speckv.h declares.
 EXPORTED = (
     "speckv_status_string", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores", "speckv_select",
-    "speckv_compact", "specpc_gather_tokens", "specpc_token_scores", "speckv_decode_workspace_bytes",
-    "speckv_decode_attention", "speckv_profile_enable", "speckv_profile_count", "speckv_profile_read",
+    "speckv_compact", "specpc_gather_tokens", "speckv_scores_rows", "speckv_compact_rows", "specpc_token_scores",
+    "speckv_decode_workspace_bytes", "speckv_decode_attention", "speckv_profile_enable", "speckv_profile_count",
+    "speckv_profile_read",
 )
 
 
@@ -66,6 +67,11 @@ def load(path: str | None = None):
                                    c_void_p]
     lib.specpc_gather_tokens.restype = c_int32
     lib.specpc_gather_tokens.argtypes = [S, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]
+    lib.speckv_scores_rows.restype = c_int32
+    lib.speckv_scores_rows.argtypes = [S, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.speckv_compact_rows.restype = c_int32
+    lib.speckv_compact_rows.argtypes = [S, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
+                                        c_void_p]
     lib.specpc_token_scores.restype = c_int32
     lib.specpc_token_scores.argtypes = [S, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]

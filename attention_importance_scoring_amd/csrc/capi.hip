@@ -266,8 +266,14 @@ skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t*
   return SKV_OK;
 }
 
-skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores, void* ws,
-                         size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// speckv_scores, with keys optionally taken through a row list (rows != NULL:
+// key j is row rows[j] of each head slab, which holds n_src_rows rows).
+skv_status scores_impl(const skv_shape* shape, const void* q_obs, const void* k, const int32_t* rows,
+                       int64_t n_src_rows, float* scores, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   SKV_TRY(check_shape(shape, &d));
   const int64_t n_obs = d.n_window + d.n_lookahead, n_pre = d.n_in - d.n_window;
@@ -300,6 +306,8 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   a.lam = reinterpret_cast<float*>(base + w.lam);
   a.colpart = reinterpret_cast<float*>(base + w.colpart);
   a.scores = scores;
+  a.key_rows = rows;
+  a.key_row_limit = (int32_t)(rows ? n_src_rows : 0);
   ScoreArgs a1 = a;  // pass 1: one unit per (layer, KV head), the whole group's rows
   a1.n_units = (int32_t)pp.units1;
   a1.n_kv_heads = (int32_t)d.Hkv;
@@ -322,6 +330,70 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
   if (a2.n_parts == 1) return SKV_OK;
   ProfScope p("colsum_combine", s);
   return hip_status(launch_colsum_combine(a2, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return scores_impl(shape, q_obs, k, nullptr, 0, scores, ws, ws_bytes, stream);
+}
+
+skv_status speckv_scores_rows(const skv_shape* shape, const void* q_obs, const void* k, const int32_t* rows,
+                              int64_t n_src_rows, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!rows) return SKV_ERR_NULL;
+  if (!aligned(rows, 4)) return SKV_ERR_ALIGN;
+  if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
+  return scores_impl(shape, q_obs, k, rows, n_src_rows, scores, ws, ws_bytes, stream);
+}
+
+skv_status speckv_compact_rows(const skv_shape* shape, const void* k, const void* v, const int32_t* rows,
+                               int64_t n_src_rows, const int32_t* kept, int64_t n_keep, void* k_out, void* v_out,
+                               void* stream) {
+  Dims d;
+  SKV_TRY(check_shape(shape, &d));
+  if (!k || !v || !rows || !kept || !k_out || !v_out) return SKV_ERR_NULL;
+  if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
+  if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4) ||
+      !aligned(rows, 4))
+    return SKV_ERR_ALIGN;
+  const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
+  const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + n_src_rows * row_bytes);
+  const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
+  const size_t kept_bytes = (size_t)(units * n_keep) * 4, rows_bytes = (size_t)d.n_in * 4;
+  if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+      ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
+      ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(kept, kept_bytes, k_out, out_bytes) ||
+      ranges_overlap(kept, kept_bytes, v_out, out_bytes) || ranges_overlap(rows, rows_bytes, k_out, out_bytes) ||
+      ranges_overlap(rows, rows_bytes, v_out, out_bytes))
+    return SKV_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GatherArgs g{};
+  g.n_units = (int32_t)units;
+  g.units_per_layer = (int32_t)d.heads();
+  g.src_units_per_layer = (int32_t)d.Hkv;
+  g.src_repeat = (int32_t)d.repeat();
+  g.n_rows = (int32_t)n_keep;
+  g.n_src_rows = (int32_t)n_src_rows;
+  g.row_bytes = (int32_t)row_bytes;
+  g.src_unit_stride = d.stride * d.esize;
+  g.dst_unit_stride = n_keep * row_bytes;
+  g.idx = kept;
+  g.idx_unit_stride = n_keep;
+  g.idx2 = rows;
+  g.n_idx2 = (int32_t)d.n_in;
+  ProfScope p("compact_gather", s);
+  g.src = k;
+  g.dst = k_out;
+  SKV_TRY(hip_status(launch_gather(g, s)));
+  g.src = v;
+  g.dst = v_out;
+  return hip_status(launch_gather(g, s));
 }
 
 skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,

@@ -35,6 +35,8 @@ struct ScoreArgs {
   float* lam;               // combine output / pass 2 input: [n_units][R] log2-domain lse
   float* scores;            // pass 2 output: [n_units][n_keys]
   float* colpart;           // pass 2, parts 1 ..: [n_parts - 1][n_units][n_keys] column sums (or maxima)
+  const int32_t* key_rows;  // NULL, or key j is row key_rows[j] (clamped to [0, key_row_limit)) of the head slab
+  int32_t key_row_limit;
 };
 
 // Work plan of the two scoring passes for one problem size.
@@ -95,6 +97,8 @@ struct GatherArgs {
   const void* src;
   void* dst;
   const int32_t* idx;       // per-unit lists (idx_unit_stride = n_rows), one shared list (0), or nullptr
+  const int32_t* idx2;      // NULL, or a shared list the first index goes through: row idx2[idx[...]]
+  int32_t n_idx2;           // entries of idx2 (a first index outside [0, n_idx2) gives a zero row)
   int64_t idx_unit_stride;  // elements
   int64_t src_unit_stride;  // bytes
   int64_t dst_unit_stride;  // bytes

@@ -120,8 +120,10 @@ __device__ __forceinline__ void read_q_frag(const char* s_q, int rt, int lane, u
 // half row of key (kbase + 32 kt + lane % 32).  Keys at or beyond n_keys read
 // the last key's row instead (clamped address, no branch): pass 1 masks them
 // through the accumulator's initial value and pass 2 never stores their
-// columns, so their contents do not matter.
-template <typename T, int D, int KT>
+// columns, so their contents do not matter.  With a row list, key j is row
+// key_rows[j] of the head slab (clamped into the slab); ROWS selects that
+// form at compile time, so the plain kernels carry no trace of it.
+template <typename T, int D, int KT, bool ROWS>
 __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbase,
                                           u32x4 (&kst)[ScoreGeom<T, D, KT>::kKT][ScoreGeom<T, D, KT>::kNV]) {
   using Gm = ScoreGeom<T, D, KT>;
@@ -131,7 +133,8 @@ __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbas
   const char* kb = static_cast<const char*>(a.k) + (layer * a.k_layer_stride + kvh * a.k_head_stride) * Elem<T>::kBytes;
 #pragma unroll
   for (int kt = 0; kt < Gm::kKT; ++kt) {
-    const int key = min(kbase + kt * 32 + (lane % 32), a.n_keys - 1);
+    int key = min(kbase + kt * 32 + (lane % 32), a.n_keys - 1);
+    if constexpr (ROWS) key = min(max(a.key_rows[key], 0), a.key_row_limit - 1);
     const char* row = kb + (int64_t)key * Gm::RF::kRowBytes + half * Gm::RF::kHalfBytes;
 #pragma unroll
     for (int v = 0; v < Gm::kNV; ++v) kst[kt][v] = ldg16(row + v * 16);
@@ -247,7 +250,7 @@ __device__ __forceinline__ RowStat renormalize(RowStat st) {
   return {st.m + (float)e, mant};
 }
 
-template <typename T, int D, int KT>
+template <typename T, int D, int KT, bool ROWS>
 __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass1_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -283,12 +286,12 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     __syncthreads();
 
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
-    load_keys<T, D, KT>(a, unit, wave_kbase(0), kst);
+    load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(0), kst);
     bool masked = false;
     for (int it = 0; it < n_iter; ++it) {
       const IterPos cu = iter_pos(it, n_tiles, rot);
       if (cu.j == 0) {  // new sub-chunk
-        if (cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);
+        if (cu.sc > 0) load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(cu.sc), kst);
         masked = sub_masked(cu.sc);
       }
       u32x4 qf[Gm::kNV];
@@ -406,7 +409,7 @@ __device__ __forceinline__ float agg2(float x, float y) {
   return x + y;
 }
 
-template <typename T, int D, int KT, bool MAX>
+template <typename T, int D, int KT, bool MAX, bool ROWS>
 __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass2_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -449,14 +452,14 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     __syncthreads();
 
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
-    load_keys<T, D, KT>(a, unit, wave_kbase(0), kst);
+    load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(0), kst);
     float colsum[Gm::kKT];
 #pragma unroll
     for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
     int in_sum = 0;  // tiles of the current sub-chunk done
     for (int it = 0; it < n_iter; ++it) {
       const IterPos cu = iter_pos(it, n_tiles, rot);
-      if (cu.j == 0 && cu.sc > 0) load_keys<T, D, KT>(a, unit, wave_kbase(cu.sc), kst);  // new sub-chunk
+      if (cu.j == 0 && cu.sc > 0) load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(cu.sc), kst);  // new sub-chunk
       float lam[16];
       read_lam(cu.rt, lam);
       f32x16 acc[Gm::kKT];
@@ -559,27 +562,36 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <typename T, int D, int KT>
-static hipError_t launch_p1(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  hipError_t e = allow_lds(score_pass1_kernel<T, D, KT>, lds);
+// ROWS: keys through the row list (a.key_rows), a separate instance so the
+// plain kernels are unchanged.
+template <typename T, int D, int KT, bool ROWS>
+static hipError_t launch_p1_form(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  hipError_t e = allow_lds(score_pass1_kernel<T, D, KT, ROWS>, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D, KT>::kThreads);
-  score_pass1_kernel<T, D, KT><<<grid, block, lds, s>>>(a);
+  score_pass1_kernel<T, D, KT, ROWS><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int D, int KT, bool MAX>
-static hipError_t launch_p2_agg(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  hipError_t e = allow_lds(score_pass2_kernel<T, D, KT, MAX>, lds);
+template <typename T, int D, int KT>
+static hipError_t launch_p1(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  return a.key_rows ? launch_p1_form<T, D, KT, true>(a, lds, s) : launch_p1_form<T, D, KT, false>(a, lds, s);
+}
+
+template <typename T, int D, int KT, bool MAX, bool ROWS>
+static hipError_t launch_p2_form(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  hipError_t e = allow_lds(score_pass2_kernel<T, D, KT, MAX, ROWS>, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)a.n_units * a.n_chunks * a.n_parts)), block(ScoreGeom<T, D, KT>::kThreads);
-  score_pass2_kernel<T, D, KT, MAX><<<grid, block, lds, s>>>(a);
+  score_pass2_kernel<T, D, KT, MAX, ROWS><<<grid, block, lds, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int KT>
 static hipError_t launch_p2(const ScoreArgs& a, size_t lds, hipStream_t s) {
-  return a.agg_max ? launch_p2_agg<T, D, KT, true>(a, lds, s) : launch_p2_agg<T, D, KT, false>(a, lds, s);
+  if (a.key_rows)
+    return a.agg_max ? launch_p2_form<T, D, KT, true, true>(a, lds, s) : launch_p2_form<T, D, KT, false, true>(a, lds, s);
+  return a.agg_max ? launch_p2_form<T, D, KT, true, false>(a, lds, s) : launch_p2_form<T, D, KT, false, false>(a, lds, s);
 }
 
 hipError_t launch_score_pass1(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s) {

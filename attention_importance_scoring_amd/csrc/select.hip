@@ -547,10 +547,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Row gather for compaction (paper notes, "Key designs", SpecKV: the kept KV
 // pairs form the compressed cache; SpecKV-PC: the target cache over the
-// SpecPC kept tokens, one token list for every head).  One thread copies one
-// 16-byte vector; consecutive threads cover consecutive bytes of a row.
-// Source indices outside [0, n_src_rows) produce zero rows instead of
-// faulting.
+// SpecPC kept tokens, one token list for every head; or the kept rows of
+// a cache addressed through that list).  One thread copies one 16-byte
+// vector; consecutive threads cover consecutive bytes of a row.  Source
+// indices outside [0, n_src_rows) produce zero rows instead of faulting.
 
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int vpr = a.row_bytes / 16;
@@ -560,7 +560,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int64_t t = (blockIdx.x % blocks_per_unit) * 256 + threadIdx.x;
   if (unit >= a.n_units || t >= per_unit) return;
   const int row = (int)(t / vpr), col = (int)(t % vpr);
-  const int src_row = a.idx ? a.idx[unit * a.idx_unit_stride + row] : row;
+  int src_row = a.idx ? a.idx[unit * a.idx_unit_stride + row] : row;
+  if (a.idx2) src_row = (src_row >= 0 && src_row < a.n_idx2) ? a.idx2[src_row] : -1;
   // source unit: same layer, head (unit % units_per_layer) / src_repeat
   const int64_t src_unit = (unit / a.units_per_layer) * a.src_units_per_layer + (unit % a.units_per_layer) / a.src_repeat;
   char* dst = static_cast<char*>(a.dst) + unit * a.dst_unit_stride + (int64_t)row * a.row_bytes + col * 16;

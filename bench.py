@@ -50,6 +50,8 @@ def parse():
                    help="decode workload: time decode over the compacted cache, the full cache, or both")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
+    p.add_argument("--cascade-path", choices=["rows", "gather"], default="rows",
+                   help="cascade: SpecKV through the kept-token list, or on a gathered copy of the target cache")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -294,9 +296,11 @@ def bench_specpc(args, cfg, torch, skv, wl):
 
 
 def bench_cascade(args, cc, torch, skv, wl):
-    """SpecKV-PC: SpecPC token scores + selection on the draft stack, the
-    target cache gathered at the kept tokens, then SpecKV scores, selection
-    and compaction over the compressed prompt, all on one stream."""
+    """SpecKV-PC: SpecPC token scores + selection on the draft stack, then
+    SpecKV scores, selection and compaction over the compressed prompt, all
+    on one stream.  Path "rows" (default): SpecKV reads the target cache
+    through the kept-token list; "gather": the target cache is first gathered
+    at the kept tokens."""
     dev = "cuda"
     inp = wl.cascade_inputs(cc, seed=args.seed or 5, device=dev)
     torch.cuda.synchronize()
@@ -310,14 +314,17 @@ def bench_cascade(args, cc, torch, skv, wl):
                                 kv_head_stride=tg["kv_head_stride"])
     s2_shape = skv.make_shape(st2.n_layers, st2.n_q_heads, st2.n_kv_heads, st2.head_dim, st2.n_in, st2.n_window,
                               st2.n_lookahead, skv.SKV_BF16)
+    rows_shape = skv.make_shape(st2.n_layers, st2.n_q_heads, st2.n_kv_heads, st2.head_dim, st2.n_in, st2.n_window,
+                                st2.n_lookahead, skv.SKV_BF16, kv_head_stride=tg["kv_head_stride"])
+    use_rows = args.cascade_path == "rows"
     ws = torch.empty(skv.speckv_workspace_bytes(pc_shape, dr.k_top), dtype=torch.uint8, device=dev)
     ws2 = torch.empty(skv.speckv_workspace_bytes(s2_shape, st2.C_max), dtype=torch.uint8, device=dev)
     L, H, d, n_tok = st2.n_layers, st2.n_kv_heads, st2.head_dim, dr.k_top
     ts = torch.empty(dr.n_in, dtype=torch.float32, device=dev)
     ts_pooled = torch.empty_like(ts)
     tokens = torch.empty(n_tok, dtype=torch.int32, device=dev)
-    k_tok = torch.empty((L, H, n_tok, d), dtype=tg["k"].dtype, device=dev)
-    v_tok = torch.empty_like(k_tok)
+    k_tok = None if use_rows else torch.empty((L, H, n_tok, d), dtype=tg["k"].dtype, device=dev)
+    v_tok = None if use_rows else torch.empty_like(k_tok)
     n_keep = skv.speckv_n_keep(s2_shape, st2.C_max)
     scores = torch.empty((L, H, st2.n_pre), dtype=torch.float32, device=dev)
     pooled = torch.empty_like(scores)
@@ -329,10 +336,18 @@ def bench_cascade(args, cc, torch, skv, wl):
     def step():
         skv.specpc_token_scores(pc_shape, dr.l_skip, inp["draft"]["q_win"], inp["draft"]["k"], None, ts, ws, stream)
         skv.speckv_select(sel_shape, ts, dr.k_top, skv.SKV_POOL_MAX, dr.pool_kernel, tokens, ts_pooled, ws, stream)
-        skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
-        skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
-        skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
-        skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
+        if use_rows:
+            skv.speckv_scores_rows(rows_shape, tg["q_obs"], tg["k_buf"], tokens, cc.target.n_in, scores, ws2, stream)
+            skv.speckv_select(rows_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2,
+                              stream)
+            skv.speckv_compact_rows(rows_shape, tg["k_buf"], tg["v_buf"], tokens, cc.target.n_in, kept, n_keep, kc, vc,
+                                    stream)
+        else:
+            skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
+            skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
+            skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2,
+                              stream)
+            skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
 
     for _ in range(args.warmup):
         step()
@@ -361,7 +376,7 @@ def bench_cascade(args, cc, torch, skv, wl):
         "config": {"workload": cc.name, "n_in": dr.n_in, "draft_layers": dr.n_layers, "l_skip": dr.l_skip,
                    "draft_heads": [dr.n_q_heads, dr.n_kv_heads, dr.head_dim], "window": dr.window, "k_top": n_tok,
                    "target_layers": L, "target_heads": [st2.n_q_heads, H, d], "n_window": st2.n_window,
-                   "n_lookahead": st2.n_lookahead, "C_max": st2.C_max},
+                   "n_lookahead": st2.n_lookahead, "C_max": st2.C_max, "path": args.cascade_path},
         "gather_tokens_GBps": round(gather_gbs, 1) if gather_gbs else None,
         "kernels": kern,
     }, inp

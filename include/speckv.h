@@ -171,6 +171,29 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
 skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const void* v, const int32_t* tokens,
                                 int64_t n_tokens, void* k_out, void* v_out, void* stream);
 
+/* SpecKV over keys taken through a row list ("Key designs", SpecKV-PC:
+ * SpecKV on the target's cache over the prompt SpecPC kept, without first
+ * gathering that cache).  The shape describes the logical problem: n_in is
+ * the number of listed rows (the compressed prompt's tokens) and
+ * kv_head_stride the stride of the physical head slabs, each holding
+ * n_src_rows rows (n_src_rows * head_dim <= kv_head_stride).  Logical key j
+ * of every head is physical row rows[j]; rows int32 [n_in] on the device,
+ * values in [0, n_src_rows) (a value outside reads a clamped row: the
+ * results are then unspecified but memory-safe).
+ * speckv_scores_rows equals speckv_scores on the gathered cache
+ * (specpc_gather_tokens with the same list), bit for bit, with the same
+ * workspace.  speckv_compact_rows writes, out of place only,
+ *   out[t] = k[rows[kept[t]]] (and v) for t < n_keep,
+ * the kept list holding logical indices as speckv_select writes them (a
+ * logical index outside [0, n_in), or a row outside [0, n_src_rows), gives
+ * a zero row); outputs as speckv_compact's, SKV_ERR_ALIAS on any overlap. */
+skv_status speckv_scores_rows(const skv_shape* shape, const void* q_obs, const void* k, const int32_t* rows,
+                              int64_t n_src_rows, float* scores, void* workspace, size_t workspace_bytes,
+                              void* stream);
+skv_status speckv_compact_rows(const skv_shape* shape, const void* k, const void* v, const int32_t* rows,
+                               int64_t n_src_rows, const int32_t* kept, int64_t n_keep, void* k_out,
+                               void* v_out, void* stream);
+
 /* SpecPC token scores ("Key designs", SpecPC).
  * The draft's query axis has n_keys = n_in + n_lookahead - 1 positions (the
  * input tokens, then the generated draft tokens but the last; n_keys = n_in

@@ -216,6 +216,33 @@ def test_gather_tokens_validation(lib):
     assert lib.specpc_gather_tokens(None, k, v, tok, 10, ko, vo, None) == NULL
 
 
+def test_row_list_validation(lib):
+    # the logical problem has 1000 rows; the physical head slabs hold n_src_rows rows of the same stride
+    s = shape()
+    _, nbytes = _ws_bytes(lib, s)
+    sr = lambda rows, n_src: lib.speckv_scores_rows(ctypes.byref(s), P(256), P(512), rows, n_src, P(1024), P(4096),
+                                                     nbytes, None)
+    assert sr(None, 1000) == NULL
+    assert sr(P(2050), 1000) == ALIGN
+    assert sr(P(2048), 0) == SHAPE
+    assert sr(P(2048), 1001) == SHAPE  # more physical rows than the head stride holds
+    assert lib.speckv_scores_rows(None, P(256), P(512), P(2048), 1000, P(1024), P(4096), nbytes, None) == NULL
+    s1 = shape(n_window=1000)  # nothing to score: accepted without touching the device
+    assert lib.speckv_scores_rows(ctypes.byref(s1), P(256), P(512), P(2048), 1000, None, P(4096), nbytes, None) == OK
+    k, v, rows, ko, vo, kept = P(1 << 30), P(2 << 30), P(3 << 30), P(4 << 30), P(5 << 30), P(6 << 30)
+    c = lambda *a: lib.speckv_compact_rows(ctypes.byref(s), *a, None)
+    assert c(k, v, rows, 1000, kept, 0, ko, vo) == PARAM
+    assert c(k, v, rows, 1000, kept, 1001, ko, vo) == PARAM
+    assert c(k, v, None, 1000, kept, 10, ko, vo) == NULL and c(k, v, rows, 1000, None, 10, ko, vo) == NULL
+    assert c(k, v, rows, 1001, kept, 10, ko, vo) == SHAPE
+    assert c(k, v, rows, 1000, kept, 10, k, v) == ALIAS                   # no in-place form
+    assert c(k, k, rows, 1000, kept, 10, ko, vo) == ALIAS
+    assert c(k, v, P((4 << 30) + 64), 1000, kept, 10, ko, vo) == ALIAS    # row list inside K out
+    assert c(k, v, rows, 1000, P((5 << 30) + 64), 10, ko, vo) == ALIAS    # kept list inside V out
+    assert c(k, v, P((3 << 30) + 2), 1000, kept, 10, ko, vo) == ALIGN
+    assert c(k, v, rows, 1000, kept, 10, P((4 << 30) + 8), vo) == ALIGN
+
+
 def test_decode_validation(lib):
     s = shape(n_in=288, n_window=16)  # a compacted cache of 288 rows per head (G = 4)
     q, k, v, out, ws = P(1 << 30), P(2 << 30), P(3 << 30), P(4 << 30), P(5 << 30)

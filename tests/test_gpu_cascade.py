@@ -23,8 +23,10 @@ from gpu_helpers import assert_kept_matches, assert_scores_close, np64, shape_of
 pytestmark = pytest.mark.gpu
 
 
-def run_cascade(cc, inp, stream=None):
-    """SpecPC -> select -> gather -> SpecKV scores -> select -> compact, one stream."""
+def run_cascade(cc, inp, stream=None, rows=False):
+    """SpecPC -> select -> gather -> SpecKV scores -> select -> compact, one stream.
+    rows=True: no gather; SpecKV reads the target cache through the token list
+    (speckv_scores_rows, speckv_compact_rows)."""
     dr, st2 = cc.draft, cc.stage2
     dq, dk = inp["draft"]["q_win"], inp["draft"]["k"]
     tg = inp["target"]
@@ -52,10 +54,17 @@ def run_cascade(cc, inp, stream=None):
     vc = torch.empty_like(kc)
     skv.specpc_token_scores(pc_shape, dr.l_skip, dq, dk, None, ts, ws, stream)
     skv.speckv_select(sel_shape, ts, dr.k_top, skv.SKV_POOL_MAX, dr.pool_kernel, tokens, ts_pooled, ws, stream)
-    skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
-    skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
-    skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
-    skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
+    if rows:
+        rows_shape = shape_of(st2, n_layers=L, kv_head_stride=tg["kv_head_stride"])
+        n_src = cc.target.n_in
+        skv.speckv_scores_rows(rows_shape, tg["q_obs"], tg["k_buf"], tokens, n_src, scores, ws2, stream)
+        skv.speckv_select(rows_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
+        skv.speckv_compact_rows(rows_shape, tg["k_buf"], tg["v_buf"], tokens, n_src, kept, n_keep, kc, vc, stream)
+    else:
+        skv.specpc_gather_tokens(full_shape, tg["k_buf"], tg["v_buf"], tokens, n_tok, k_tok, v_tok, stream)
+        skv.speckv_scores(s2_shape, tg["q_obs"], k_tok, scores, ws2, stream)
+        skv.speckv_select(s2_shape, scores, st2.C_max, skv.SKV_POOL_MAX, st2.pool_kernel, kept, pooled, ws2, stream)
+        skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
     return {"ts": ts, "ts_pooled": ts_pooled, "tokens": tokens, "k_tok": k_tok, "v_tok": v_tok, "scores": scores,
             "pooled": pooled, "kept": kept, "k": kc, "v": vc}
 
@@ -125,6 +134,59 @@ def test_cascade_full_size_sampled():
     exact = oracle.select_kept(out["ts_pooled"].cpu().numpy().astype(np.float64), cc.draft.k_top, 0)
     assert (out["tokens"].cpu().numpy() == exact).all()
     _check_stage2(out, inp, cc, [(0, 0), (31, 4), (63, 7)])
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["small", "full-size"])
+def test_row_list_path_equals_gathered_path(full):
+    # SpecKV through the token list (no gathered cache) gives the gathered path's scores, kept lists and
+    # final cache bit for bit
+    if full:
+        cc, seed = wl.CASCADES["speckv_pc_cascade_32k"], 5
+    else:
+        base = wl.CASCADES["speckv_pc_cascade_32k"]
+        cc = wl.CascadeConfig("cascade_small",
+                              wl.reduced(base.draft, n_layers=6, l_skip=2, n_in=3000, window=128, k_top=400),
+                              wl.reduced(base.target, n_layers=3, n_in=3000, n_lookahead=16, C_max=50))
+        seed = 11
+    print(f"\n[case] {cc.name}: row-list path against the gathered path", flush=True)
+    inp = wl.cascade_inputs(cc, seed, "cuda")
+    a = run_cascade(cc, inp)
+    b = run_cascade(cc, inp, rows=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a["tokens"], b["tokens"])
+    for key in ("scores", "pooled", "kept", "k", "v"):
+        assert torch.equal(a[key], b[key]), f"{key} differs between the row-list and the gathered path"
+
+
+def test_compact_rows_out_of_range_gives_zero_rows():
+    # rows[kept[t]]: a kept index outside [0, n_in) or a listed row outside [0, n_src_rows) gives a zero row
+    L, Hq, Hkv, d, n_src, n_in = 2, 8, 2, 128, 500, 6
+    print(f"\n[case] compact_rows: {L} layers x {Hkv} heads, {n_in} listed rows of {n_src}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(23)
+    stride = n_src * d
+    kb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    vb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    rows = torch.tensor([499, 3, 250, -2, 500, 7], dtype=torch.int32, device="cuda")
+    kept = torch.tensor([0, 1, 2, 3, 4, 5, 6, -1], dtype=torch.int32, device="cuda").repeat(L, Hkv, 1).contiguous()
+    n_keep = kept.shape[-1]
+    shape = skv.make_shape(L, Hq, Hkv, d, n_in, 0, 0, skv.SKV_BF16, kv_head_stride=stride)
+    with pytest.raises(skv.SpecKVError):  # n_keep above n_in
+        skv.speckv_compact_rows(shape, kb, vb, rows, n_src, kept, n_keep, kb, vb)
+    shape = skv.make_shape(L, Hq, Hkv, d, n_keep, 0, 0, skv.SKV_BF16, kv_head_stride=stride)
+    rows8 = torch.cat([rows, torch.tensor([1, 2], dtype=torch.int32, device="cuda")])
+    kc = torch.full((L, Hkv, n_keep, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, 7.0)
+    kept6 = kept.clone()
+    kept6[..., 6] = 8  # beyond the 8 listed rows
+    skv.speckv_compact_rows(shape, kb, vb, rows8, n_src, kept6, n_keep, kc, vc)
+    torch.cuda.synchronize()
+    k3 = kb.view(L, Hkv, n_src, d)
+    v3 = vb.view(L, Hkv, n_src, d)
+    for t, r in enumerate([499, 3, 250, None, None, 7, None, None]):
+        if r is None:
+            assert (kc[:, :, t] == 0).all() and (vc[:, :, t] == 0).all(), f"slot {t} should be a zero row"
+        else:
+            assert torch.equal(kc[:, :, t], k3[:, :, r]) and torch.equal(vc[:, :, t], v3[:, :, r])
 
 
 def test_gather_tokens_ragged_list_and_out_of_range_tokens():
