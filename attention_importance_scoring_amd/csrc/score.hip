@@ -11,12 +11,13 @@
 //
 // Work split: one block per CU (8 waves; 12 at head_dim 64, where the vector
 // work dominates) owns a chunk of consecutive keys of one unit (layer, KV
-// head, or query head when each has its own kept set) and one "part" of the
-// unit's query rows: as many 32-row tiles as fit in LDS (up to ~156 KB),
-// copied there once.  The parts
-// of a chunk are neighbouring blocks on one XCD, so K comes from HBM about
-// once and from L2 for the other parts; pass 2 writes one column-sum row per
-// part and a small kernel adds them in part order.  Every wave walks its
+// head, or, in pass 2, query head when each has its own kept set) and one
+// "part" of the unit's query rows: as many 32-row tiles as fit in LDS (up to
+// ~156 KB), copied there once.  The parts of a chunk are neighbouring blocks
+// on one XCD, so K comes from HBM about once and from L2 for the other parts
+// (in pass 1 every part walks the same number of tiles to stay in step);
+// pass 2 writes one column-sum row per part and a small kernel adds them in
+// part order.  Keys may also be read through a row list (the ROWS instances).  Every wave walks its
 // share of the chunk, kKT tiles of 32 keys at a time held in registers as an
 // MFMA operand, against every row tile of the part.  The main loop has no
 // barriers: the rows are read-only in LDS, each wave keeps its own row
