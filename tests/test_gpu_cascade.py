@@ -158,6 +158,52 @@ def test_row_list_path_equals_gathered_path(full):
         assert torch.equal(a[key], b[key]), f"{key} differs between the row-list and the gathered path"
 
 
+@pytest.mark.parametrize("agg,pqh,d", [("max", 0, 128), ("sum", 1, 128), ("max", 1, 64), ("sum", 0, 64)])
+def test_row_list_variants_equal_gathered(agg, pqh, d):
+    # speckv_scores_rows / speckv_compact_rows against speckv_scores / speckv_compact on the gathered rows,
+    # bit for bit, with max aggregation, one kept set per query head and head_dim 64
+    L, Hq, Hkv, n_src, n_list, n_window, n_look, C_max = 2, 8, 2, 3000, 1100, 32, 64, 100
+    print(f"\n[case] row list: aggregation {agg}, per_query_head {pqh}, d {d}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(29 + pqh + d)
+    stride = n_src * d
+    kb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    vb = torch.randn((L, Hkv, stride), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((L, Hq, n_window + n_look, d), generator=g, device="cuda").to(torch.bfloat16)
+    rows = torch.sort(torch.randperm(n_src, generator=g, device="cuda")[:n_list])[0].int()
+    aggc = skv.SKV_AGG_MAX if agg == "max" else skv.SKV_AGG_SUM
+    rshape = skv.make_shape(L, Hq, Hkv, d, n_list, n_window, n_look, skv.SKV_BF16, kv_head_stride=stride,
+                            aggregation=aggc, per_query_head=pqh)
+    gshape = skv.make_shape(L, Hq, Hkv, d, n_list, n_window, n_look, skv.SKV_BF16, aggregation=aggc,
+                            per_query_head=pqh)
+    fshape = skv.make_shape(L, Hq, Hkv, d, n_src, 0, 0, skv.SKV_BF16, kv_head_stride=stride)
+    kg = torch.empty((L, Hkv, n_list, d), dtype=torch.bfloat16, device="cuda")
+    vg = torch.empty_like(kg)
+    skv.specpc_gather_tokens(fshape, kb, vb, rows, n_list, kg, vg)
+    H = Hq if pqh else Hkv
+    n_pre, n_keep = n_list - n_window, skv.speckv_n_keep(rshape, C_max)
+    out = {}
+    for name, shape in (("rows", rshape), ("gathered", gshape)):
+        ws = torch.empty(skv.speckv_workspace_bytes(shape, C_max), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((L, H, n_pre), device="cuda")
+        kept = torch.empty((L, H, n_keep), dtype=torch.int32, device="cuda")
+        kc = torch.empty((L, H, n_keep, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        if name == "rows":
+            skv.speckv_scores_rows(shape, q, kb, rows, n_src, sc, ws)
+            skv.speckv_select(shape, sc, C_max, skv.SKV_POOL_MAX, 7, kept, None, ws)
+            skv.speckv_compact_rows(shape, kb, vb, rows, n_src, kept, n_keep, kc, vc)
+        else:
+            skv.speckv_scores(shape, q, kg, sc, ws)
+            skv.speckv_select(shape, sc, C_max, skv.SKV_POOL_MAX, 7, kept, None, ws)
+            skv.speckv_compact(shape, kg, vg, kept, n_keep, kc, vc, ws)
+        out[name] = (sc, kept, kc, vc)
+    torch.cuda.synchronize()
+    for a, b, what in zip(out["rows"], out["gathered"], ("scores", "kept", "K", "V")):
+        assert torch.equal(a, b), f"{what} differs between the row-list and the gathered path"
+    want = oracle.speckv_scores(np64(q), np64(kg), n_window, aggregation=agg, per_query_head=bool(pqh))
+    assert_scores_close(out["rows"][0].cpu().numpy(), want, 1 if pqh else Hq // Hkv, n_window + n_look)
+
+
 def test_compact_rows_out_of_range_gives_zero_rows():
     # rows[kept[t]]: a kept index outside [0, n_in) or a listed row outside [0, n_src_rows) gives a zero row
     L, Hq, Hkv, d, n_src, n_in = 2, 8, 2, 128, 500, 6
