@@ -467,7 +467,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the scoring path is per-GPU work with no collectives "
-              "(see DESIGN.md for how it would shard); rerun with --gpus 1", file=sys.stderr)
+              "(units are independent, so a GPU's share is the same launch over fewer layers); "
+              "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import attention_importance_scoring_amd as skv
