@@ -6,11 +6,11 @@ bytes it produces.  Generation runs on any torch device (on the GPU for the
 large workloads, which are then copied to the host for the oracle).
 
 Workload shapes follow the models the paper notes ("Draft-based Approximate
-Inference for LLMs", sections "Background" and "Main experiments", Table 1)
-evaluate: a Llama-3.1-8B-shaped target (32 layers, 32 query / 8 KV heads,
-head_dim 128), a Qwen2.5-32B-shaped target (64 layers, 40 / 8 heads,
-head_dim 128) and a Qwen2.5-0.5B-class draft (24 layers, 14 / 2 heads,
-head_dim 64).  The pages' LongBench / RULER workloads are replaced by the
+Inference for LLMs", sections "Background", "Main experiments" with Table 1,
+and "Limitations") name: a Llama-3.1-8B-shaped target (32 layers, 32 query /
+8 KV heads, head_dim 128), a Qwen2.5-32B-shaped target (64 layers, 40 / 8
+heads, head_dim 128) and a Qwen2.5-0.5B-class draft (24 layers, 14 / 2
+heads, head_dim 64).  The pages' LongBench / RULER workloads are replaced by the
 synthetic key distributions below:
 
 * heavy hitters: a key k_j = beta * sqrt(d) * u + noise, with u the unit mean

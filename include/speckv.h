@@ -76,9 +76,10 @@ typedef enum skv_agg { SKV_AGG_SUM = 0, SKV_AGG_MAX = 1 } skv_agg;
  * Query head hq uses KV head hq / G, G = n_q_heads / n_kv_heads.
  * SpecKV scores, selects and compacts per "head" h < H, where H = n_kv_heads
  * (one kept set per KV head, shared by its G query heads; the default) or
- * H = n_q_heads with per_query_head = 1 (the key designs paragraph scores
- * "each attention head"; query head hq is scored alone against KV head
- * hq / G, and its compacted cache holds rows of that KV head). */
+ * H = n_q_heads with per_query_head = 1 (the key designs paragraph
+ * estimates importance per attention head; query head hq is scored alone
+ * against KV head hq / G, and its compacted cache holds rows of that KV
+ * head). */
 typedef struct skv_shape {
   int32_t n_layers;       /* >= 1                                                   */
   int32_t n_q_heads;      /* multiple of n_kv_heads                                 */

@@ -94,9 +94,9 @@ def speckv_scores(q_obs, k, n_window: int, scale: float | None = None, aggregati
     Returns float64 [L, Hkv, n_pre], or [L, Hq, n_pre] with per_query_head,
     where query head hq is scored alone against its KV head's keys.
 
-    Reading (per_query_head): the pages estimate importance "for each
-    attention head"; the default keeps one set per KV head, shared by its
-    query heads, and this variant keeps one per query head.
+    Reading (per_query_head): the pages estimate importance per attention
+    head; the default keeps one set per KV head, shared by its query heads,
+    and this variant keeps one per query head.
     """
     L, Hq, _, d = q_obs.shape
     Lk, Hkv, n_in, dk = k.shape
