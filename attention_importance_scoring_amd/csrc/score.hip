@@ -43,6 +43,14 @@ constexpr int kScoreLdsBudget = 156 * 1024;  // dynamic LDS per block (one block
 #define SKV_TARGET_BLOCKS 768
 #endif
 constexpr int kMaxSubPerChunk = SKV_MAX_SUB;  // groups of resident keys per block
+// With two waves per SIMD, the wave that reads its row fragment and issues
+// its MFMAs runs at raised issue priority, so the matrix unit is fed first
+// and the other wave's exp/sum work takes the remaining issue cycles.  (At
+// three waves per SIMD, head_dim 64, it gained nothing and is not used.)
+template <int P>
+__device__ __forceinline__ void mfma_prio() {
+  __builtin_amdgcn_s_setprio(P);
+}
 
 template <typename T, int D, int KT>
 struct ScoreGeom {
@@ -296,6 +304,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         masked = sub_masked(cu.sc);
       }
       u32x4 qf[Gm::kNV];
+      if constexpr (Gm::kWaves == 8) mfma_prio<1>();
       read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
       f32x16 acc[Gm::kKT];
       const int r = cu.rt * 32 + lane % 32;
@@ -303,6 +312,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         pass1_mfma<T, D, KT, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
       else
         pass1_mfma<T, D, KT, false>(kst, qf, 0, acc);
+      if constexpr (Gm::kWaves == 8) mfma_prio<0>();
       RowStat st;
       if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
         st = masked ? pass1_stats<T, D, KT, true>(acc, c) : pass1_stats<T, D, KT, false>(acc, c);
@@ -465,8 +475,10 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
       read_lam(cu.rt, lam);
       f32x16 acc[Gm::kKT];
       u32x4 qf[Gm::kNV];
+      if constexpr (Gm::kWaves == 8) mfma_prio<1>();
       read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
       pass2_mfma<T, D, KT>(kst, qf, acc);
+      if constexpr (Gm::kWaves == 8) mfma_prio<0>();
       // acc[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
 #pragma unroll
       for (int kt = 0; kt < Gm::kKT; ++kt) {
