@@ -21,7 +21,7 @@
 namespace skv {
 
 #ifndef SKV_PC_RT
-#define SKV_PC_RT 1
+#define SKV_PC_RT 2
 #endif
 #ifndef SKV_PC_WAVES
 #define SKV_PC_WAVES 8
@@ -67,7 +67,7 @@ __device__ __forceinline__ void specpc_pass2_block(const SpecPCArgs& pa, int rb,
   const ScoreArgs& a = pa.sc;
   const int mps = pa.maps_per_stage;
   char* s_rows = smem;                                                          // [2][mps][kMapBytes]
-  float* s_lam = reinterpret_cast<float*>(smem + (size_t)2 * mps * Gm::kMapBytes);  // [2][mps][64]
+  float* s_lam = reinterpret_cast<float*>(smem + (size_t)2 * mps * Gm::kMapBytes);  // [2][mps][kRowsPerBlock]
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, half = lane / 32;
   const int W = a.rows_per_qhead, G = a.group;
   const int row0 = rb * Gm::kRowsPerBlock;                    // first window row of the block
