@@ -15,6 +15,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libspeckv.so")
+PEAKS_SRC = os.path.join(PKG_DIR, "peaks", "peaks.hip")
+PEAKS_BIN = os.path.join(PKG_DIR, "peaks", "skv_peaks")  # measured unit ceilings, a separate program
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -59,7 +61,20 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH} from {len(sources)} sources")
+    build_peaks(verbose)
     return LIB_PATH
+
+
+def build_peaks(verbose: bool = True) -> str:
+    tmp = PEAKS_BIN + ".tmp"
+    r = subprocess.run([hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"], PEAKS_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}:\n{r.stderr}")
+    os.replace(tmp, PEAKS_BIN)
+    if verbose:
+        print(f"built {PEAKS_BIN}")
+    return PEAKS_BIN
 
 
 if __name__ == "__main__":
