@@ -25,6 +25,9 @@ METRIC = "keys scored+compacted/sec and % of HBM/MFMA roofline at n_in=64K, 32B 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# v_exp_f32: 256 CUs x 32 exponentials per clock (one wave64 instruction per 8 cycles on each of the 4 SIMDs)
+# x 2.4 GHz; the peak-check program measures 17.4 T/s, about 9 cycles per instruction.
+PEAK_EXP_TPS = 256 * 32 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -132,6 +135,33 @@ def decode_cpu_baseline(cfg, inp, cache, budget_s=10.0):
             "sample": f"{done} unit decodes over {len(units)} distinct (layer, KV head) units of {n_rows} rows "
                       f"(the first rows of the full cache stand in for the compacted ones), {t_total:.1f} s of "
                       f"fp64 NumPy, scaled to all {L * H} units of one decode step"}
+
+
+def specpc_cpu_baseline(cfg, inp, budget_s=12.0):
+    """The fp64 oracle's SpecPC token scores one used layer at a time (all
+    its query heads), until ~budget_s of work, scaled to every used layer,
+    plus its pooling and selection once."""
+    import oracle
+    from attention_importance_scoring_amd import workloads as wl
+    used = list(range(cfg.l_skip, cfg.n_layers))
+    done, t_layers, scores = 0, 0.0, None
+    for layer in used:
+        q = wl.to_numpy_f64(inp["q_win"][layer:layer + 1])
+        k = wl.to_numpy_f64(inp["k"][layer:layer + 1])
+        t0 = time.perf_counter()
+        scores = oracle.specpc_token_scores(q, k, 0, n_in=cfg.n_in)
+        t_layers += time.perf_counter() - t0
+        done += 1
+        if t_layers >= budget_s:
+            break
+    t0 = time.perf_counter()
+    oracle.specpc_select(scores, cfg.k_top, "max", cfg.pool_kernel)
+    t_sel = time.perf_counter() - t0
+    per_step = t_layers / done * len(used) + t_sel
+    return {"value": cfg.n_in / per_step, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{done} of {len(used)} used layers ({done * cfg.n_q_heads} causal window maps of "
+                      f"{cfg.window} x {cfg.n_keys}), {t_layers:.1f} s of fp64 NumPy, scaled to all used layers, "
+                      f"plus pooling and selection ({t_sel:.2f} s)"}
 
 
 def traffic_for(kernel: str, workload: str, summary: str):
@@ -284,6 +314,13 @@ def bench_specpc(args, cfg, torch, skv, wl):
     maps = (cfg.n_layers - cfg.l_skip) * cfg.n_q_heads
     elems = maps * sum(min(cfg.n_keys, cfg.n_keys - cfg.window + i + 1) for i in range(cfg.window))
     exps_per_s = 2 * elems / (ms * 1e-3)  # two passes, one exp per (row, visible key) each
+    # Both passes evaluate one exponential per (map, window row, visible key): the exp roofline of the longer one.
+    dom = max(("score_pass1", "specpc_pass2"), key=lambda k: kern.get(k, {}).get("avg_ms", 0.0))
+    achieved = elems / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    default_cfg = args.n_lookahead is None
+    roof = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_EXP_TPS, 2),
+            "unit": "T exp/s", "frac": round(achieved / PEAK_EXP_TPS, 4),
+            "traffic": traffic_for(dom, cfg.name, f"specpc_kernels_{cfg.name}_traffic.json") if default_cfg else None}
     return {
         "metric": "SpecPC tokens scored+selected/sec (draft attention stack)", "value": cfg.n_in / (ms * 1e-3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -291,7 +328,7 @@ def bench_specpc(args, cfg, torch, skv, wl):
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "l_skip": cfg.l_skip, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "n_in": cfg.n_in, "window": cfg.window,
                    "n_lookahead": cfg.n_lookahead, "k_top": cfg.k_top},
-        "exp_rate_per_s": exps_per_s, "kernels": kern,
+        "roofline": roof, "exp_rate_per_s": exps_per_s, "kernels": kern,
     }, inp
 
 
@@ -497,7 +534,11 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n * 4
-    if not args.no_cpu_baseline and args.workload == "decode_qwen32b_shape_64k":
+    if not args.no_cpu_baseline and args.workload == "specpc_draft_32k":
+        print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
+        pc_cfg = wl.reduced(cfg, n_lookahead=args.n_lookahead) if args.n_lookahead is not None else cfg
+        out["cpu_baseline"] = specpc_cpu_baseline(pc_cfg, inp)
+    elif not args.no_cpu_baseline and args.workload == "decode_qwen32b_shape_64k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = decode_cpu_baseline(cfg, inp, args.decode_cache)
     elif not args.no_cpu_baseline and args.workload in wl.WORKLOADS \
