@@ -137,10 +137,11 @@ def decode_cpu_baseline(cfg, inp, cache, budget_s=10.0):
                       f"fp64 NumPy, scaled to all {L * H} units of one decode step"}
 
 
-def specpc_cpu_baseline(cfg, inp, budget_s=12.0):
-    """The fp64 oracle's SpecPC token scores one used layer at a time (all
-    its query heads), until ~budget_s of work, scaled to every used layer,
-    plus its pooling and selection once."""
+def _specpc_oracle_time(cfg, inp, budget_s):
+    """Seconds per step of the fp64 oracle's SpecPC token scores and selection:
+    one used layer at a time (all its query heads) until ~budget_s, scaled
+    to every used layer.  Returns (seconds, layers timed, used layers,
+    selection seconds, kept tokens)."""
     import oracle
     from attention_importance_scoring_amd import workloads as wl
     used = list(range(cfg.l_skip, cfg.n_layers))
@@ -155,13 +156,60 @@ def specpc_cpu_baseline(cfg, inp, budget_s=12.0):
         if t_layers >= budget_s:
             break
     t0 = time.perf_counter()
-    oracle.specpc_select(scores, cfg.k_top, "max", cfg.pool_kernel)
+    tokens, _ = oracle.specpc_select(scores, cfg.k_top, "max", cfg.pool_kernel)
     t_sel = time.perf_counter() - t0
-    per_step = t_layers / done * len(used) + t_sel
+    return t_layers / done * len(used) + t_sel, done, len(used), t_sel, tokens
+
+
+def specpc_cpu_baseline(cfg, inp, budget_s=12.0):
+    """The fp64 oracle's SpecPC token scores one used layer at a time (all
+    its query heads), until ~budget_s of work, scaled to every used layer,
+    plus its pooling and selection once."""
+    per_step, done, n_used, t_sel, _ = _specpc_oracle_time(cfg, inp, budget_s)
     return {"value": cfg.n_in / per_step, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{done} of {len(used)} used layers ({done * cfg.n_q_heads} causal window maps of "
-                      f"{cfg.window} x {cfg.n_keys}), {t_layers:.1f} s of fp64 NumPy, scaled to all used layers, "
-                      f"plus pooling and selection ({t_sel:.2f} s)"}
+            "sample": f"{done} of {n_used} used layers ({done * cfg.n_q_heads} causal window maps of "
+                      f"{cfg.window} x {cfg.n_keys}), about {budget_s:.0f} s of fp64 NumPy, scaled to all used "
+                      f"layers, plus pooling and selection ({t_sel:.2f} s)"}
+
+
+def cascade_cpu_baseline(cc, inp, budget_s=12.0):
+    """The fp64 oracle's cascade: SpecPC on the draft as in
+    specpc_cpu_baseline (half the budget), then SpecKV on the compressed
+    prompt over whole (layer, KV head) units of the target, gathering the
+    kept tokens' rows, scoring, pooling, selecting and compacting (the
+    other half), scaled to all units."""
+    import numpy as np
+    import torch
+    import oracle
+    from attention_importance_scoring_amd import workloads as wl
+    dr, tg = cc.draft, cc.target
+    pc_s, pc_done, pc_used, _, tokens = _specpc_oracle_time(dr, inp["draft"], budget_s / 2)
+    t_in = inp["target"]
+    G, n_tok = tg.n_q_heads // tg.n_kv_heads, len(tokens)
+    units = [(l, h) for l in range(tg.n_layers) for h in range(tg.n_kv_heads)]
+    order = np.random.default_rng(0).permutation(len(units))
+    done, t_units = 0, 0.0
+    for idx in order:
+        l, h = units[idx]
+        q = wl.to_numpy_f64(t_in["q_obs"][l, h * G:(h + 1) * G])
+        k = wl.to_numpy_f64(t_in["k"][l, h])
+        v = t_in["v"][l, h].cpu()
+        v_raw = v.view(torch.int16).numpy() if v.dtype == torch.bfloat16 else v.numpy()  # bit copy
+        t0 = time.perf_counter()
+        k_c, v_c = k[tokens], v_raw[tokens]
+        s = oracle.head_scores(q, k_c[:n_tok - tg.n_window], oracle.default_scale(tg.head_dim))
+        kept = oracle.select_kept(oracle.pool1d(s, tg.pool_kernel, "max"), tg.C_max, tg.n_window)
+        oracle.compact_rows(k_c, kept)
+        oracle.compact_rows(v_c, kept)
+        t_units += time.perf_counter() - t0
+        done += 1
+        if t_units >= budget_s / 2:
+            break
+    per_step = pc_s + t_units / done * len(units)
+    return {"value": dr.n_in / per_step, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"SpecPC: {pc_done} of {pc_used} used draft layers, scaled to all; SpecKV on the "
+                      f"{n_tok}-token prompt: {done} of {len(units)} (layer, KV head) units, scaled to all; "
+                      f"about {budget_s:.0f} s of fp64 NumPy in total"}
 
 
 def traffic_for(kernel: str, workload: str, summary: str):
@@ -401,6 +449,13 @@ def bench_cascade(args, cc, torch, skv, wl):
     skv.profile_enable(False)
     kern = {name: {"launches": n, "avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
             for name, (n, t) in prof.items()}
+    # The longest launch is SpecPC's pass 2 on the draft: its exp roofline, as in the SpecPC workload.
+    pc_maps = (dr.n_layers - dr.l_skip) * dr.n_q_heads
+    pc_elems = pc_maps * sum(min(dr.n_keys, dr.n_keys - dr.window + i + 1) for i in range(dr.window))
+    pc_ach = pc_elems / (kern["specpc_pass2"]["avg_ms"] * 1e-3) / 1e12
+    roof = {"kernel": "specpc_pass2", "bound": "alu", "achieved": round(pc_ach, 3), "peak": round(PEAK_EXP_TPS, 2),
+            "unit": "T exp/s", "frac": round(pc_ach / PEAK_EXP_TPS, 4),
+            "traffic": traffic_for("specpc_pass2", cc.name, f"cascade_kernels_{cc.name}_traffic.json")}
     # the gather moves n_tok rows of K and V per (layer, KV head) in and out
     g = kern.get("gather_tokens")
     gather_bytes = 2 * 2 * L * H * n_tok * d * 2  # K and V, read and write, bf16
@@ -415,7 +470,7 @@ def bench_cascade(args, cc, torch, skv, wl):
                    "target_layers": L, "target_heads": [st2.n_q_heads, H, d], "n_window": st2.n_window,
                    "n_lookahead": st2.n_lookahead, "C_max": st2.C_max, "path": args.cascade_path},
         "gather_tokens_GBps": round(gather_gbs, 1) if gather_gbs else None,
-        "kernels": kern,
+        "roofline": roof, "kernels": kern,
     }, inp
 
 
@@ -534,7 +589,10 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n * 4
-    if not args.no_cpu_baseline and args.workload == "specpc_draft_32k":
+    if not args.no_cpu_baseline and args.workload in wl.CASCADES:
+        print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cascade_cpu_baseline(wl.CASCADES[args.workload], inp)
+    elif not args.no_cpu_baseline and args.workload == "specpc_draft_32k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         pc_cfg = wl.reduced(cfg, n_lookahead=args.n_lookahead) if args.n_lookahead is not None else cfg
         out["cpu_baseline"] = specpc_cpu_baseline(pc_cfg, inp)
