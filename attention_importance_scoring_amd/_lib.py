@@ -14,7 +14,7 @@ c_int32, c_int64, c_float, c_size_t, c_void_p = ctypes.c_int32, ctypes.c_int64, 
 
 STATUS_NAMES = {
     0: "SKV_OK", 1: "SKV_ERR_NULL", 2: "SKV_ERR_SHAPE", 3: "SKV_ERR_DTYPE", 4: "SKV_ERR_PARAM",
-    5: "SKV_ERR_WORKSPACE", 6: "SKV_ERR_ALIGN", 7: "SKV_ERR_ALIAS", 8: "SKV_ERR_HIP",
+    5: "SKV_ERR_WORKSPACE", 6: "SKV_ERR_ALIGN", 7: "SKV_ERR_ALIAS", 8: "SKV_ERR_HIP", 9: "SKV_ERR_INTERNAL",
 }
 SKV_F32, SKV_BF16 = 0, 1
 SKV_POOL_NONE, SKV_POOL_MAX, SKV_POOL_AVG = 0, 1, 2

@@ -135,6 +135,15 @@ PcWs specpc_ws(const Dims& d, int64_t units) {
   return w;
 }
 
+// Workspace of specpc_token_scores for any l_skip: the planner may give fewer
+// units (a larger l_skip) more key chunks, hence larger pass-1 partials, so
+// the size is the maximum over every l_skip in [0, L).
+size_t specpc_ws_any_lskip(const Dims& d) {
+  size_t need = 0;
+  for (int64_t ls = 0; ls < d.L; ++ls) need = std::max(need, specpc_ws(d, (d.L - ls) * d.Hkv).end);
+  return need;
+}
+
 int64_t keep_count(const Dims& d, int64_t C_max) {
   const int64_t n_pre = d.n_in - d.n_window;
   return (C_max < n_pre ? C_max : n_pre) + d.n_window;
@@ -166,27 +175,48 @@ hipEvent_t take_event() {
   return e;
 }
 
+// Returns an event to the spare list, or destroys it when the list cannot grow.
+void give_event(hipEvent_t e) {
+  try {
+    g_spare.push_back(e);
+  } catch (...) {
+    (void)hipEventDestroy(e);
+  }
+}
+
+// The profiling lists grow while profiling is on; a host allocation failure
+// drops that sample and marks the profile incomplete instead of throwing
+// (the scope's destructor runs inside the C ABI).
+bool g_prof_lost = false;
+
 struct ProfScope {
   int entry = -1;
   hipEvent_t start = nullptr;
   hipStream_t stream;
   ProfScope(const char* name, hipStream_t s) : stream(s) {
     if (!g_prof_on) return;
-    for (size_t i = 0; i < g_prof.size(); ++i)
-      if (std::strcmp(g_prof[i].name, name) == 0) entry = (int)i;
-    if (entry < 0) {
-      g_prof.push_back({name, 0, 0.0});
-      entry = (int)g_prof.size() - 1;
+    try {
+      for (size_t i = 0; i < g_prof.size(); ++i)
+        if (std::strcmp(g_prof[i].name, name) == 0) entry = (int)i;
+      if (entry < 0) {
+        g_prof.push_back({name, 0, 0.0});
+        entry = (int)g_prof.size() - 1;
+      }
+      g_pending.reserve(g_pending.size() + 1);
+    } catch (...) {
+      g_prof_lost = true;
+      entry = -1;
+      return;
     }
     start = take_event();
     if (start) (void)hipEventRecord(start, stream);
   }
   ~ProfScope() {
-    if (!g_prof_on || !start) return;
+    if (!g_prof_on || !start || entry < 0) return;
     hipEvent_t stop = take_event();
     if (!stop) return;
     (void)hipEventRecord(stop, stream);
-    g_pending.push_back({entry, start, stop});
+    g_pending.push_back({entry, start, stop});  // capacity reserved by the constructor: does not throw
   }
 };
 
@@ -222,6 +252,23 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Every extern "C" body runs through this: a C++ exception (a host
+// allocation failure in the library or the HIP runtime) becomes a status.
+template <typename F>
+skv_status guard(F&& body) {
+  try {
+    return body();
+  } catch (...) {
+    return SKV_ERR_INTERNAL;
+  }
+}
+
+// Bytes spanned by the K (or V) buffer: every head slab but the last in full,
+// then the rows of the last one.
+size_t kv_span(const Dims& d, int64_t rows_last) {
+  return (size_t)((d.L * d.Hkv - 1) * d.stride * d.esize + rows_last * d.D * d.esize);
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,33 +284,38 @@ const char* speckv_status_string(skv_status status) {
     case SKV_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case SKV_ERR_ALIAS: return "output overlaps an input";
     case SKV_ERR_HIP: return "HIP runtime error";
+    case SKV_ERR_INTERNAL: return "host-side failure inside the library";
   }
   return "unknown status";
 }
 
 skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!out) return SKV_ERR_NULL;
-  if (C_max < 0) return SKV_ERR_PARAM;
-  *out = keep_count(d, C_max);
-  return SKV_OK;
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!out) return SKV_ERR_NULL;
+    if (C_max < 0) return SKV_ERR_PARAM;
+    *out = keep_count(d, C_max);
+    return SKV_OK;
+  });
 }
 
 skv_status speckv_workspace_bytes(const skv_shape* shape, int32_t C_max, size_t* out) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!out) return SKV_ERR_NULL;
-  if (C_max < 0) return SKV_ERR_PARAM;
-  const int64_t units = d.L * d.heads();
-  const int64_t n_pre = d.n_in - d.n_window;
-  size_t need = speckv_plans(d, n_pre).ws.end;                                               // speckv_scores
-  need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)) +                   // speckv_select
-                            select_candidate_bytes(units, n_pre, keep_count(d, C_max) - d.n_window));
-  need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
-  if (d.n_window >= 1) need = std::max(need, specpc_ws(d, d.L * d.Hkv).end);                   // specpc_token_scores
-  *out = need;
-  return SKV_OK;
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!out) return SKV_ERR_NULL;
+    if (C_max < 0) return SKV_ERR_PARAM;
+    const int64_t units = d.L * d.heads();
+    const int64_t n_pre = d.n_in - d.n_window;
+    size_t need = speckv_plans(d, n_pre).ws.end;                                               // speckv_scores
+    need = std::max(need, round_up((size_t)(units * n_pre) * sizeof(float)) +                   // speckv_select
+                              select_candidate_bytes(units, n_pre, keep_count(d, C_max) - d.n_window));
+    need = std::max(need, 2 * round_up((size_t)(units * keep_count(d, C_max) * d.D * d.esize)));  // in-place compact
+    if (d.n_window >= 1) need = std::max(need, specpc_ws_any_lskip(d));                          // specpc_token_scores
+    *out = need;
+    return SKV_OK;
+  });
 }
 
 }  // extern "C"
@@ -286,6 +338,14 @@ skv_status scores_impl(const skv_shape* shape, const void* q_obs, const void* k,
   if (n_pre == 0) return SKV_OK;
   if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+  const size_t q_bytes = (size_t)(d.L * d.Hq * n_obs * d.D * d.esize);
+  const size_t k_bytes = kv_span(d, rows ? n_src_rows : d.n_in);
+  const size_t s_bytes = (size_t)(d.L * d.heads() * n_pre) * sizeof(float);
+  if (ranges_overlap(scores, s_bytes, q_obs, q_bytes) || ranges_overlap(scores, s_bytes, k, k_bytes) ||
+      ranges_overlap(scores, s_bytes, ws, w.end) || ranges_overlap(ws, w.end, q_obs, q_bytes) ||
+      ranges_overlap(ws, w.end, k, k_bytes) || (rows && ranges_overlap(rows, (size_t)d.n_in * 4, scores, s_bytes)) ||
+      (rows && ranges_overlap(rows, (size_t)d.n_in * 4, ws, w.end)))
+    return SKV_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ScoreArgs a{};
   a.q = q_obs;
@@ -338,297 +398,318 @@ extern "C" {
 
 skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores, void* ws,
                          size_t ws_bytes, void* stream) {
-  return scores_impl(shape, q_obs, k, nullptr, 0, scores, ws, ws_bytes, stream);
+  return guard([&]() -> skv_status {
+    return scores_impl(shape, q_obs, k, nullptr, 0, scores, ws, ws_bytes, stream);
+  });
 }
 
 skv_status speckv_scores_rows(const skv_shape* shape, const void* q_obs, const void* k, const int32_t* rows,
                               int64_t n_src_rows, float* scores, void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!rows) return SKV_ERR_NULL;
-  if (!aligned(rows, 4)) return SKV_ERR_ALIGN;
-  if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
-  return scores_impl(shape, q_obs, k, rows, n_src_rows, scores, ws, ws_bytes, stream);
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!rows) return SKV_ERR_NULL;
+    if (!aligned(rows, 4)) return SKV_ERR_ALIGN;
+    if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
+    return scores_impl(shape, q_obs, k, rows, n_src_rows, scores, ws, ws_bytes, stream);
+  });
 }
 
 skv_status speckv_compact_rows(const skv_shape* shape, const void* k, const void* v, const int32_t* rows,
                                int64_t n_src_rows, const int32_t* kept, int64_t n_keep, void* k_out, void* v_out,
                                void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!k || !v || !rows || !kept || !k_out || !v_out) return SKV_ERR_NULL;
-  if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
-  if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4) ||
-      !aligned(rows, 4))
-    return SKV_ERR_ALIGN;
-  const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
-  const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + n_src_rows * row_bytes);
-  const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
-  const size_t kept_bytes = (size_t)(units * n_keep) * 4, rows_bytes = (size_t)d.n_in * 4;
-  if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
-      ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
-      ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(kept, kept_bytes, k_out, out_bytes) ||
-      ranges_overlap(kept, kept_bytes, v_out, out_bytes) || ranges_overlap(rows, rows_bytes, k_out, out_bytes) ||
-      ranges_overlap(rows, rows_bytes, v_out, out_bytes))
-    return SKV_ERR_ALIAS;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  GatherArgs g{};
-  g.n_units = (int32_t)units;
-  g.units_per_layer = (int32_t)d.heads();
-  g.src_units_per_layer = (int32_t)d.Hkv;
-  g.src_repeat = (int32_t)d.repeat();
-  g.n_rows = (int32_t)n_keep;
-  g.n_src_rows = (int32_t)n_src_rows;
-  g.row_bytes = (int32_t)row_bytes;
-  g.src_unit_stride = d.stride * d.esize;
-  g.dst_unit_stride = n_keep * row_bytes;
-  g.idx = kept;
-  g.idx_unit_stride = n_keep;
-  g.idx2 = rows;
-  g.n_idx2 = (int32_t)d.n_in;
-  ProfScope p("compact_gather", s);
-  g.src = k;
-  g.dst = k_out;
-  SKV_TRY(hip_status(launch_gather(g, s)));
-  g.src = v;
-  g.dst = v_out;
-  return hip_status(launch_gather(g, s));
-}
-
-skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,
-                         int32_t* kept, float* pooled, void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!kept || (!scores && d.n_in > d.n_window)) return SKV_ERR_NULL;  // an empty prefix has no scores
-  if (C_max < 0) return SKV_ERR_PARAM;
-  if (pool != SKV_POOL_NONE && pool != SKV_POOL_MAX && pool != SKV_POOL_AVG) return SKV_ERR_PARAM;
-  if (pool != SKV_POOL_NONE && (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 4097)) return SKV_ERR_PARAM;
-  if (!aligned(scores, 4) || !aligned(kept, 4) || (pooled && !aligned(pooled, 4))) return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.heads(), n_pre = d.n_in - d.n_window;
-  const int64_t n_keep = keep_count(d, C_max);
-  if (pooled && ranges_overlap(pooled, (size_t)(units * n_pre) * 4, scores, (size_t)(units * n_pre) * 4))
-    return SKV_ERR_ALIAS;
-  if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, scores, (size_t)(units * n_pre) * 4)) return SKV_ERR_ALIAS;
-  const int64_t n_top = n_keep - d.n_window;
-  const int n_seg = select_segments(units, n_pre, n_top);
-  const size_t pool_bytes = pooled ? 0 : round_up((size_t)(units * n_pre) * sizeof(float));
-  const size_t cand_bytes = select_candidate_bytes(units, n_pre, n_top);
-  float* pl = pooled;
-  char* cand = nullptr;
-  if (pool_bytes + cand_bytes > 0) {
-    if (!ws || ws_bytes < pool_bytes + cand_bytes) return SKV_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
-    if (!pooled) pl = static_cast<float*>(ws);
-    cand = static_cast<char*>(ws) + pool_bytes;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  SelectArgs a{};
-  a.n_seg = n_seg;
-  a.seg_len = (int32_t)((n_pre + n_seg - 1) / n_seg);
-  if (n_seg > 1) {
-    a.cand_key = reinterpret_cast<uint32_t*>(cand);
-    a.cand_idx = reinterpret_cast<int32_t*>(cand + (size_t)(units * n_seg * n_top) * 4);
-  }
-  a.scores = scores;
-  a.pooled = pl;
-  a.kept = kept;
-  a.n_units = (int32_t)units;
-  a.n_pre = (int32_t)n_pre;
-  a.n_window = (int32_t)d.n_window;
-  a.n_top = (int32_t)n_top;
-  a.pool = pool;
-  a.pool_radius = pool == SKV_POOL_NONE ? 0 : pool_kernel / 2;
-  a.write_pooled = pooled != nullptr;
-  ProfScope p("select", s);
-  return hip_status(launch_select(a, s));
-}
-
-skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, const int32_t* kept, int64_t n_keep,
-                          void* k_out, void* v_out, void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!k || !v || !kept || !k_out || !v_out) return SKV_ERR_NULL;
-  if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4))
-    return SKV_ERR_ALIGN;
-  const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
-  const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + d.n_in * row_bytes);
-  const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
-  const bool k_inplace = (k_out == k), v_inplace = (v_out == v);
-  if (k_inplace != v_inplace) return SKV_ERR_ALIAS;
-  if (k == v) return SKV_ERR_ALIAS;
-  if (k_inplace && units != kv_units) return SKV_ERR_PARAM;  // per-query-head caches do not fit the KV slabs
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  GatherArgs g{};
-  g.n_units = (int32_t)units;
-  g.units_per_layer = (int32_t)d.heads();
-  g.src_units_per_layer = (int32_t)d.Hkv;
-  g.src_repeat = (int32_t)d.repeat();
-  g.n_rows = (int32_t)n_keep;
-  g.n_src_rows = (int32_t)d.n_in;
-  g.row_bytes = (int32_t)row_bytes;
-  g.src_unit_stride = d.stride * d.esize;
-  if (!k_inplace) {
-    if (ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!k || !v || !rows || !kept || !k_out || !v_out) return SKV_ERR_NULL;
+    if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
+    if (n_src_rows < 1 || n_src_rows > INT32_MAX || n_src_rows * d.D > d.stride) return SKV_ERR_SHAPE;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4) ||
+        !aligned(rows, 4))
+      return SKV_ERR_ALIGN;
+    const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
+    const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + n_src_rows * row_bytes);
+    const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
+    const size_t kept_bytes = (size_t)(units * n_keep) * 4, rows_bytes = (size_t)d.n_in * 4;
+    if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
         ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
-        ranges_overlap(k_out, out_bytes, v_out, out_bytes) ||
-        ranges_overlap(kept, (size_t)(units * n_keep) * 4, k_out, out_bytes) ||
-        ranges_overlap(kept, (size_t)(units * n_keep) * 4, v_out, out_bytes))
+        ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(kept, kept_bytes, k_out, out_bytes) ||
+        ranges_overlap(kept, kept_bytes, v_out, out_bytes) || ranges_overlap(rows, rows_bytes, k_out, out_bytes) ||
+        ranges_overlap(rows, rows_bytes, v_out, out_bytes))
       return SKV_ERR_ALIAS;
-    ProfScope p("compact_gather", s);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GatherArgs g{};
+    g.n_units = (int32_t)units;
+    g.units_per_layer = (int32_t)d.heads();
+    g.src_units_per_layer = (int32_t)d.Hkv;
+    g.src_repeat = (int32_t)d.repeat();
+    g.n_rows = (int32_t)n_keep;
+    g.n_src_rows = (int32_t)n_src_rows;
+    g.row_bytes = (int32_t)row_bytes;
+    g.src_unit_stride = d.stride * d.esize;
+    g.dst_unit_stride = n_keep * row_bytes;
     g.idx = kept;
     g.idx_unit_stride = n_keep;
-    g.dst_unit_stride = n_keep * row_bytes;
+    g.idx2 = rows;
+    g.n_idx2 = (int32_t)d.n_in;
+    ProfScope p("compact_gather", s);
     g.src = k;
     g.dst = k_out;
     SKV_TRY(hip_status(launch_gather(g, s)));
     g.src = v;
     g.dst = v_out;
     return hip_status(launch_gather(g, s));
-  }
-  // In place: gather K and V into the workspace, then copy back to rows [0, n_keep).
-  if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, k, in_bytes) ||
-      ranges_overlap(kept, (size_t)(units * n_keep) * 4, v, in_bytes) || ranges_overlap(k, in_bytes, v, in_bytes))
-    return SKV_ERR_ALIAS;
-  const size_t stage = round_up(out_bytes);
-  if (!ws || ws_bytes < 2 * stage) return SKV_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
-  if (ranges_overlap(ws, 2 * stage, k, in_bytes) || ranges_overlap(ws, 2 * stage, v, in_bytes)) return SKV_ERR_ALIAS;
-  char* ks = static_cast<char*>(ws);
-  char* vs = ks + stage;
-  {
-    ProfScope p("compact_gather", s);
-    g.idx = kept;
-    g.idx_unit_stride = n_keep;
-    g.dst_unit_stride = n_keep * row_bytes;
-    g.src = k;
-    g.dst = ks;
-    SKV_TRY(hip_status(launch_gather(g, s)));
-    g.src = v;
-    g.dst = vs;
-    SKV_TRY(hip_status(launch_gather(g, s)));
-  }
-  ProfScope p("compact_copyback", s);
-  GatherArgs b{};
-  b.n_units = (int32_t)units;
-  b.units_per_layer = b.src_units_per_layer = (int32_t)d.Hkv;
-  b.src_repeat = 1;
-  b.n_rows = (int32_t)n_keep;
-  b.n_src_rows = (int32_t)n_keep;
-  b.row_bytes = (int32_t)row_bytes;
-  b.idx = nullptr;
-  b.src_unit_stride = n_keep * row_bytes;
-  b.dst_unit_stride = d.stride * d.esize;
-  b.src = ks;
-  b.dst = const_cast<void*>(k);
-  SKV_TRY(hip_status(launch_gather(b, s)));
-  b.src = vs;
-  b.dst = const_cast<void*>(v);
-  return hip_status(launch_gather(b, s));
+  });
+}
+
+skv_status speckv_select(const skv_shape* shape, const float* scores, int32_t C_max, int32_t pool, int32_t pool_kernel,
+                         int32_t* kept, float* pooled, void* ws, size_t ws_bytes, void* stream) {
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!kept || (!scores && d.n_in > d.n_window)) return SKV_ERR_NULL;  // an empty prefix has no scores
+    if (C_max < 0) return SKV_ERR_PARAM;
+    if (pool != SKV_POOL_NONE && pool != SKV_POOL_MAX && pool != SKV_POOL_AVG) return SKV_ERR_PARAM;
+    if (pool != SKV_POOL_NONE && (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 4097)) return SKV_ERR_PARAM;
+    if (!aligned(scores, 4) || !aligned(kept, 4) || (pooled && !aligned(pooled, 4))) return SKV_ERR_ALIGN;
+    const int64_t units = d.L * d.heads(), n_pre = d.n_in - d.n_window;
+    const int64_t n_keep = keep_count(d, C_max);
+    const size_t s_bytes = (size_t)(units * n_pre) * 4, kept_bytes = (size_t)(units * n_keep) * 4;
+    if (pooled && ranges_overlap(pooled, s_bytes, scores, s_bytes)) return SKV_ERR_ALIAS;
+    if (pooled && ranges_overlap(pooled, s_bytes, kept, kept_bytes)) return SKV_ERR_ALIAS;
+    if (ranges_overlap(kept, kept_bytes, scores, s_bytes)) return SKV_ERR_ALIAS;
+    const int64_t n_top = n_keep - d.n_window;
+    const int n_seg = select_segments(units, n_pre, n_top);
+    const size_t pool_bytes = pooled ? 0 : round_up((size_t)(units * n_pre) * sizeof(float));
+    const size_t cand_bytes = select_candidate_bytes(units, n_pre, n_top);
+    float* pl = pooled;
+    char* cand = nullptr;
+    if (pool_bytes + cand_bytes > 0) {
+      if (!ws || ws_bytes < pool_bytes + cand_bytes) return SKV_ERR_WORKSPACE;
+      if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+      const size_t used = pool_bytes + cand_bytes;
+      if (ranges_overlap(ws, used, scores, s_bytes) || ranges_overlap(ws, used, kept, kept_bytes) ||
+          (pooled && ranges_overlap(ws, used, pooled, s_bytes)))
+        return SKV_ERR_ALIAS;
+      if (!pooled) pl = static_cast<float*>(ws);
+      cand = static_cast<char*>(ws) + pool_bytes;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SelectArgs a{};
+    a.n_seg = n_seg;
+    a.seg_len = (int32_t)((n_pre + n_seg - 1) / n_seg);
+    if (n_seg > 1) {
+      a.cand_key = reinterpret_cast<uint32_t*>(cand);
+      a.cand_idx = reinterpret_cast<int32_t*>(cand + (size_t)(units * n_seg * n_top) * 4);
+    }
+    a.scores = scores;
+    a.pooled = pl;
+    a.kept = kept;
+    a.n_units = (int32_t)units;
+    a.n_pre = (int32_t)n_pre;
+    a.n_window = (int32_t)d.n_window;
+    a.n_top = (int32_t)n_top;
+    a.pool = pool;
+    a.pool_radius = pool == SKV_POOL_NONE ? 0 : pool_kernel / 2;
+    a.write_pooled = pooled != nullptr;
+    ProfScope p("select", s);
+    return hip_status(launch_select(a, s));
+  });
+}
+
+skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, const int32_t* kept, int64_t n_keep,
+                          void* k_out, void* v_out, void* ws, size_t ws_bytes, void* stream) {
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!k || !v || !kept || !k_out || !v_out) return SKV_ERR_NULL;
+    if (n_keep < 1 || n_keep > d.n_in) return SKV_ERR_PARAM;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(kept, 4))
+      return SKV_ERR_ALIGN;
+    const int64_t kv_units = d.L * d.Hkv, units = d.L * d.heads(), row_bytes = d.D * d.esize;
+    const size_t in_bytes = (size_t)((kv_units - 1) * d.stride * d.esize + d.n_in * row_bytes);
+    const size_t out_bytes = (size_t)(units * n_keep * row_bytes);
+    const bool k_inplace = (k_out == k), v_inplace = (v_out == v);
+    if (k_inplace != v_inplace) return SKV_ERR_ALIAS;
+    if (k == v) return SKV_ERR_ALIAS;
+    if (k_inplace && units != kv_units) return SKV_ERR_PARAM;  // per-query-head caches do not fit the KV slabs
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GatherArgs g{};
+    g.n_units = (int32_t)units;
+    g.units_per_layer = (int32_t)d.heads();
+    g.src_units_per_layer = (int32_t)d.Hkv;
+    g.src_repeat = (int32_t)d.repeat();
+    g.n_rows = (int32_t)n_keep;
+    g.n_src_rows = (int32_t)d.n_in;
+    g.row_bytes = (int32_t)row_bytes;
+    g.src_unit_stride = d.stride * d.esize;
+    if (!k_inplace) {
+      if (ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+          ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
+          ranges_overlap(k_out, out_bytes, v_out, out_bytes) ||
+          ranges_overlap(kept, (size_t)(units * n_keep) * 4, k_out, out_bytes) ||
+          ranges_overlap(kept, (size_t)(units * n_keep) * 4, v_out, out_bytes))
+        return SKV_ERR_ALIAS;
+      ProfScope p("compact_gather", s);
+      g.idx = kept;
+      g.idx_unit_stride = n_keep;
+      g.dst_unit_stride = n_keep * row_bytes;
+      g.src = k;
+      g.dst = k_out;
+      SKV_TRY(hip_status(launch_gather(g, s)));
+      g.src = v;
+      g.dst = v_out;
+      return hip_status(launch_gather(g, s));
+    }
+    // In place: gather K and V into the workspace, then copy back to rows [0, n_keep).
+    if (ranges_overlap(kept, (size_t)(units * n_keep) * 4, k, in_bytes) ||
+        ranges_overlap(kept, (size_t)(units * n_keep) * 4, v, in_bytes) || ranges_overlap(k, in_bytes, v, in_bytes))
+      return SKV_ERR_ALIAS;
+    const size_t stage = round_up(out_bytes);
+    if (!ws || ws_bytes < 2 * stage) return SKV_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+    if (ranges_overlap(ws, 2 * stage, k, in_bytes) || ranges_overlap(ws, 2 * stage, v, in_bytes) ||
+        ranges_overlap(ws, 2 * stage, kept, (size_t)(units * n_keep) * 4))
+      return SKV_ERR_ALIAS;
+    char* ks = static_cast<char*>(ws);
+    char* vs = ks + stage;
+    {
+      ProfScope p("compact_gather", s);
+      g.idx = kept;
+      g.idx_unit_stride = n_keep;
+      g.dst_unit_stride = n_keep * row_bytes;
+      g.src = k;
+      g.dst = ks;
+      SKV_TRY(hip_status(launch_gather(g, s)));
+      g.src = v;
+      g.dst = vs;
+      SKV_TRY(hip_status(launch_gather(g, s)));
+    }
+    ProfScope p("compact_copyback", s);
+    GatherArgs b{};
+    b.n_units = (int32_t)units;
+    b.units_per_layer = b.src_units_per_layer = (int32_t)d.Hkv;
+    b.src_repeat = 1;
+    b.n_rows = (int32_t)n_keep;
+    b.n_src_rows = (int32_t)n_keep;
+    b.row_bytes = (int32_t)row_bytes;
+    b.idx = nullptr;
+    b.src_unit_stride = n_keep * row_bytes;
+    b.dst_unit_stride = d.stride * d.esize;
+    b.src = ks;
+    b.dst = const_cast<void*>(k);
+    SKV_TRY(hip_status(launch_gather(b, s)));
+    b.src = vs;
+    b.dst = const_cast<void*>(v);
+    return hip_status(launch_gather(b, s));
+  });
 }
 
 skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const void* v, const int32_t* tokens,
                                 int64_t n_tokens, void* k_out, void* v_out, void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!k || !v || !tokens || !k_out || !v_out) return SKV_ERR_NULL;
-  if (n_tokens < 1 || n_tokens > d.n_in) return SKV_ERR_PARAM;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(tokens, 4))
-    return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.Hkv, row_bytes = d.D * d.esize;
-  const size_t in_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * row_bytes);
-  const size_t out_bytes = (size_t)(units * n_tokens * row_bytes);
-  const size_t tok_bytes = (size_t)n_tokens * 4;
-  if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
-      ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
-      ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(tokens, tok_bytes, k_out, out_bytes) ||
-      ranges_overlap(tokens, tok_bytes, v_out, out_bytes))
-    return SKV_ERR_ALIAS;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  GatherArgs g{};
-  g.n_units = (int32_t)units;
-  g.units_per_layer = g.src_units_per_layer = (int32_t)d.Hkv;
-  g.src_repeat = 1;
-  g.n_rows = (int32_t)n_tokens;
-  g.n_src_rows = (int32_t)d.n_in;
-  g.row_bytes = (int32_t)row_bytes;
-  g.src_unit_stride = d.stride * d.esize;
-  g.dst_unit_stride = n_tokens * row_bytes;
-  g.idx = tokens;
-  g.idx_unit_stride = 0;  // one token list for every (layer, KV head)
-  ProfScope p("gather_tokens", s);
-  g.src = k;
-  g.dst = k_out;
-  SKV_TRY(hip_status(launch_gather(g, s)));
-  g.src = v;
-  g.dst = v_out;
-  return hip_status(launch_gather(g, s));
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!k || !v || !tokens || !k_out || !v_out) return SKV_ERR_NULL;
+    if (n_tokens < 1 || n_tokens > d.n_in) return SKV_ERR_PARAM;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(tokens, 4))
+      return SKV_ERR_ALIGN;
+    const int64_t units = d.L * d.Hkv, row_bytes = d.D * d.esize;
+    const size_t in_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * row_bytes);
+    const size_t out_bytes = (size_t)(units * n_tokens * row_bytes);
+    const size_t tok_bytes = (size_t)n_tokens * 4;
+    if (k == v || ranges_overlap(k_out, out_bytes, k, in_bytes) || ranges_overlap(k_out, out_bytes, v, in_bytes) ||
+        ranges_overlap(v_out, out_bytes, k, in_bytes) || ranges_overlap(v_out, out_bytes, v, in_bytes) ||
+        ranges_overlap(k_out, out_bytes, v_out, out_bytes) || ranges_overlap(tokens, tok_bytes, k_out, out_bytes) ||
+        ranges_overlap(tokens, tok_bytes, v_out, out_bytes))
+      return SKV_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GatherArgs g{};
+    g.n_units = (int32_t)units;
+    g.units_per_layer = g.src_units_per_layer = (int32_t)d.Hkv;
+    g.src_repeat = 1;
+    g.n_rows = (int32_t)n_tokens;
+    g.n_src_rows = (int32_t)d.n_in;
+    g.row_bytes = (int32_t)row_bytes;
+    g.src_unit_stride = d.stride * d.esize;
+    g.dst_unit_stride = n_tokens * row_bytes;
+    g.idx = tokens;
+    g.idx_unit_stride = 0;  // one token list for every (layer, KV head)
+    ProfScope p("gather_tokens", s);
+    g.src = k;
+    g.dst = k_out;
+    SKV_TRY(hip_status(launch_gather(g, s)));
+    g.src = v;
+    g.dst = v_out;
+    return hip_status(launch_gather(g, s));
+  });
 }
 
 skv_status specpc_token_scores(const skv_shape* shape, int32_t l_skip, const void* q_win, const void* k,
                                const float* query_weights, float* token_scores, void* ws, size_t ws_bytes,
                                void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!q_win || !k || !token_scores) return SKV_ERR_NULL;
-  if (l_skip < 0 || l_skip >= d.L) return SKV_ERR_PARAM;
-  if (d.agg != SKV_AGG_SUM || d.pqh) return SKV_ERR_PARAM;  // SpecPC has its own aggregation
-  const int64_t W = d.n_window;
-  if (W < 1) return SKV_ERR_SHAPE;
-  if ((d.Hq / d.Hkv) * W > kMaxRows) return SKV_ERR_SHAPE;
-  if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(token_scores, 4) ||
-      (query_weights && !aligned(query_weights, 4)))
-    return SKV_ERR_ALIGN;
-  const int64_t G = d.Hq / d.Hkv, units = (d.L - l_skip) * d.Hkv;
-  const int64_t n_keys = specpc_keys(d);  // keys in the causal normaliser
-  if (d.stride < n_keys * d.D) return SKV_ERR_SHAPE;  // head slabs must hold the draft keys too
-  const PcWs w = specpc_ws(d, units);
-  if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  SpecPCArgs pa{};
-  ScoreArgs& a = pa.sc;
-  a.q = q_win;
-  a.k = k;
-  a.q_head_stride = W * d.D;
-  a.q_layer_stride = d.Hq * a.q_head_stride;
-  a.k_head_stride = d.stride;
-  a.k_layer_stride = d.Hkv * d.stride;
-  a.layer0 = l_skip;
-  a.n_units = (int32_t)units;
-  a.n_kv_heads = (int32_t)d.Hkv;
-  a.kv_repeat = 1;
-  a.agg_max = 0;
-  a.group = (int32_t)G;
-  a.rows_per_qhead = (int32_t)W;
-  a.n_rows = (int32_t)(G * W);
-  a.n_keys = (int32_t)n_keys;
-  ScorePlan pl;
-  score_plan(d.dtype, (int)d.D, units, G * W, n_keys, &pl);
-  apply_plan(a, pl);
-  a.causal = 1;
-  a.pos_base = n_keys - W;  // window row i sits at position n_keys - W + i
-  a.c = d.scale * 1.4426950408889634f;
-  char* base = static_cast<char*>(ws);
-  a.part = reinterpret_cast<float2*>(base + w.sc.part);
-  a.lam = reinterpret_cast<float*>(base + w.sc.lam);
-  a.scores = nullptr;
-  a.colpart = nullptr;
-  pa.weights = query_weights;
-  pa.rowblock_max = reinterpret_cast<float*>(base + w.rowmax);
-  pa.token_scores = token_scores;
-  const int rpb = specpc_rows_per_block(d.dtype, (int)d.D);
-  pa.n_rowblocks = (int32_t)((W + rpb - 1) / rpb);
-  pa.inv_maps = (float)(1.0 / (double)(units * G));
-  SKV_TRY(run_scoring(d, a, pl, s));
-  a.n_keys = (int32_t)d.n_in;  // the mean and max cover the input tokens only
-  {
-    ProfScope p("specpc_pass2", s);
-    SKV_TRY(hip_status(launch_specpc_pass2(d.dtype, (int)d.D, pa, s)));
-  }
-  ProfScope p("specpc_reduce", s);
-  return hip_status(launch_specpc_reduce(pa, s));
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!q_win || !k || !token_scores) return SKV_ERR_NULL;
+    if (l_skip < 0 || l_skip >= d.L) return SKV_ERR_PARAM;
+    if (d.agg != SKV_AGG_SUM || d.pqh) return SKV_ERR_PARAM;  // SpecPC has its own aggregation
+    const int64_t W = d.n_window;
+    if (W < 1) return SKV_ERR_SHAPE;
+    if ((d.Hq / d.Hkv) * W > kMaxRows) return SKV_ERR_SHAPE;
+    if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(token_scores, 4) ||
+        (query_weights && !aligned(query_weights, 4)))
+      return SKV_ERR_ALIGN;
+    const int64_t G = d.Hq / d.Hkv, units = (d.L - l_skip) * d.Hkv;
+    const int64_t n_keys = specpc_keys(d);  // keys in the causal normaliser
+    if (d.stride < n_keys * d.D) return SKV_ERR_SHAPE;  // head slabs must hold the draft keys too
+    const PcWs w = specpc_ws(d, units);
+    if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SpecPCArgs pa{};
+    ScoreArgs& a = pa.sc;
+    a.q = q_win;
+    a.k = k;
+    a.q_head_stride = W * d.D;
+    a.q_layer_stride = d.Hq * a.q_head_stride;
+    a.k_head_stride = d.stride;
+    a.k_layer_stride = d.Hkv * d.stride;
+    a.layer0 = l_skip;
+    a.n_units = (int32_t)units;
+    a.n_kv_heads = (int32_t)d.Hkv;
+    a.kv_repeat = 1;
+    a.agg_max = 0;
+    a.group = (int32_t)G;
+    a.rows_per_qhead = (int32_t)W;
+    a.n_rows = (int32_t)(G * W);
+    a.n_keys = (int32_t)n_keys;
+    ScorePlan pl;
+    score_plan(d.dtype, (int)d.D, units, G * W, n_keys, &pl);
+    apply_plan(a, pl);
+    a.causal = 1;
+    a.pos_base = n_keys - W;  // window row i sits at position n_keys - W + i
+    a.c = d.scale * 1.4426950408889634f;
+    char* base = static_cast<char*>(ws);
+    a.part = reinterpret_cast<float2*>(base + w.sc.part);
+    a.lam = reinterpret_cast<float*>(base + w.sc.lam);
+    a.scores = nullptr;
+    a.colpart = nullptr;
+    pa.weights = query_weights;
+    pa.rowblock_max = reinterpret_cast<float*>(base + w.rowmax);
+    pa.token_scores = token_scores;
+    const int rpb = specpc_rows_per_block(d.dtype, (int)d.D);
+    pa.n_rowblocks = (int32_t)((W + rpb - 1) / rpb);
+    pa.inv_maps = (float)(1.0 / (double)(units * G));
+    SKV_TRY(run_scoring(d, a, pl, s));
+    a.n_keys = (int32_t)d.n_in;  // the mean and max cover the input tokens only
+    {
+      ProfScope p("specpc_pass2", s);
+      SKV_TRY(hip_status(launch_specpc_pass2(d.dtype, (int)d.D, pa, s)));
+    }
+    ProfScope p("specpc_reduce", s);
+    return hip_status(launch_specpc_reduce(pa, s));
+  });
 }
 
 size_t decode_ws_bytes(const Dims& d, int64_t n_rows) {
@@ -641,88 +722,105 @@ size_t decode_ws_bytes(const Dims& d, int64_t n_rows) {
 }
 
 skv_status speckv_decode_workspace_bytes(const skv_shape* shape, int64_t n_rows, size_t* out_bytes) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!out_bytes) return SKV_ERR_NULL;
-  if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
-  *out_bytes = decode_ws_bytes(d, n_rows);
-  return SKV_OK;
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!out_bytes) return SKV_ERR_NULL;
+    if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
+    *out_bytes = decode_ws_bytes(d, n_rows);
+    return SKV_OK;
+  });
 }
 
 skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const void* q, const void* k,
                                    const void* v, float* out, void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  SKV_TRY(check_shape(shape, &d));
-  if (!q || !k || !v || !out) return SKV_ERR_NULL;
-  if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
-  if (d.group() > decode_max_group()) return SKV_ERR_SHAPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4)) return SKV_ERR_ALIGN;
-  const int64_t units = d.L * d.heads();
-  const size_t cache_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * d.D * d.esize);
-  const size_t out_bytes = (size_t)(d.L * d.Hq * d.D) * sizeof(float);
-  if (ranges_overlap(out, out_bytes, q, (size_t)(d.L * d.Hq * d.D * d.esize)) ||
-      ranges_overlap(out, out_bytes, k, cache_bytes) || ranges_overlap(out, out_bytes, v, cache_bytes))
-    return SKV_ERR_ALIAS;
-  const size_t need = decode_ws_bytes(d, n_rows);
-  DecodeArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.head_stride = d.stride;
-  a.n_rows = n_rows;
-  a.n_units = (int32_t)units;
-  a.heads_per_layer = (int32_t)d.heads();
-  a.q_heads_per_layer = (int32_t)d.Hq;
-  a.group = (int32_t)d.group();
-  decode_plan(d.dtype, units, n_rows, &a.n_sub, &a.n_chunks);
-  a.c = d.scale * 1.4426950408889634f;
-  a.out = out;
-  if (need > 0) {
-    if (!ws || ws_bytes < need) return SKV_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
-    if (ranges_overlap(ws, need, out, out_bytes) || ranges_overlap(ws, need, k, cache_bytes) ||
-        ranges_overlap(ws, need, v, cache_bytes))
+  return guard([&]() -> skv_status {
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (!q || !k || !v || !out) return SKV_ERR_NULL;
+    if (n_rows < 1 || n_rows > d.n_in) return SKV_ERR_PARAM;
+    if (d.group() > decode_max_group()) return SKV_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4)) return SKV_ERR_ALIGN;
+    const int64_t units = d.L * d.heads();
+    const size_t cache_bytes = (size_t)((units - 1) * d.stride * d.esize + d.n_in * d.D * d.esize);
+    const size_t out_bytes = (size_t)(d.L * d.Hq * d.D) * sizeof(float);
+    if (ranges_overlap(out, out_bytes, q, (size_t)(d.L * d.Hq * d.D * d.esize)) ||
+        ranges_overlap(out, out_bytes, k, cache_bytes) || ranges_overlap(out, out_bytes, v, cache_bytes))
       return SKV_ERR_ALIAS;
-    const int64_t slots = units * a.n_chunks * decode_max_group();
-    a.part_ml = static_cast<float2*>(ws);
-    a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)slots * sizeof(float2)));
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  ProfScope p("decode_attention", s);
-  return hip_status(launch_decode_attention(d.dtype, (int)d.D, a, s));
+    const size_t need = decode_ws_bytes(d, n_rows);
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.head_stride = d.stride;
+    a.n_rows = n_rows;
+    a.n_units = (int32_t)units;
+    a.heads_per_layer = (int32_t)d.heads();
+    a.q_heads_per_layer = (int32_t)d.Hq;
+    a.group = (int32_t)d.group();
+    decode_plan(d.dtype, units, n_rows, &a.n_sub, &a.n_chunks);
+    a.c = d.scale * 1.4426950408889634f;
+    a.out = out;
+    if (need > 0) {
+      if (!ws || ws_bytes < need) return SKV_ERR_WORKSPACE;
+      if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+      if (ranges_overlap(ws, need, out, out_bytes) || ranges_overlap(ws, need, k, cache_bytes) ||
+          ranges_overlap(ws, need, v, cache_bytes))
+        return SKV_ERR_ALIAS;
+      const int64_t slots = units * a.n_chunks * decode_max_group();
+      a.part_ml = static_cast<float2*>(ws);
+      a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)slots * sizeof(float2)));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope p("decode_attention", s);
+    return hip_status(launch_decode_attention(d.dtype, (int)d.D, a, s));
+  });
 }
 
 skv_status speckv_profile_enable(int32_t on) {
-  if (on) {
-    g_prof.clear();
-    for (auto& p : g_pending) {
-      g_spare.push_back(p.start);
-      g_spare.push_back(p.stop);
+  return guard([&]() -> skv_status {
+    if (on) {
+      g_prof.clear();
+      for (auto& p : g_pending) {
+        give_event(p.start);
+        give_event(p.stop);
+      }
+      g_pending.clear();
+      g_prof_lost = false;
     }
-    g_pending.clear();
-  }
-  g_prof_on = on != 0;
-  return SKV_OK;
+    g_prof_on = on != 0;
+    return SKV_OK;
+  });
 }
 
 int32_t speckv_profile_count(void) { return (int32_t)g_prof.size(); }
 
 skv_status speckv_profile_read(int32_t index, const char** name, int64_t* launches, double* total_ms) {
-  for (auto& p : g_pending) {
-    if (hipEventSynchronize(p.stop) != hipSuccess) return SKV_ERR_HIP;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) return SKV_ERR_HIP;
-    g_prof[p.entry].launches += 1;
-    g_prof[p.entry].ms += ms;
-    g_spare.push_back(p.start);
-    g_spare.push_back(p.stop);
-  }
-  g_pending.clear();
-  if (index < 0 || index >= (int32_t)g_prof.size()) return SKV_ERR_PARAM;
-  if (name) *name = g_prof[index].name;
-  if (launches) *launches = g_prof[index].launches;
-  if (total_ms) *total_ms = g_prof[index].ms;
-  return SKV_OK;
+  return guard([&]() -> skv_status {
+    // Samples are folded into the totals in order; one that cannot be read
+    // yet stays pending (the ones before it are not counted twice).
+    size_t done = 0;
+    skv_status st = SKV_OK;
+    for (; done < g_pending.size(); ++done) {
+      const ProfPending& p = g_pending[done];
+      float ms = 0.f;
+      if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {
+        st = SKV_ERR_HIP;
+        break;
+      }
+      g_prof[p.entry].launches += 1;
+      g_prof[p.entry].ms += ms;
+      give_event(p.start);
+      give_event(p.stop);
+    }
+    g_pending.erase(g_pending.begin(), g_pending.begin() + (std::ptrdiff_t)done);
+    if (st != SKV_OK) return st;
+    if (index < 0 || index >= (int32_t)g_prof.size()) return SKV_ERR_PARAM;
+    if (name) *name = g_prof[index].name;
+    if (launches) *launches = g_prof[index].launches;
+    if (total_ms) *total_ms = g_prof[index].ms;
+    return g_prof_lost ? SKV_ERR_INTERNAL : SKV_OK;  // dropped samples: the totals are incomplete
+  });
 }
 
 }  // extern "C"

@@ -28,7 +28,11 @@
  *     stream.
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing is launched and the outputs are untouched.  No C++
- *     exception crosses this interface.
+ *     exception crosses this interface: every entry point catches them and
+ *     returns SKV_ERR_INTERNAL.
+ *   - The library keeps no state between calls except the optional
+ *     event-timing lists of speckv_profile_* (host memory, process-wide,
+ *     empty unless profiling is enabled).
  *   - NaN or Inf inputs give undefined (but memory-safe) results.
  *   - Element types: SKV_F32 (float) or SKV_BF16 (bfloat16 stored as
  *     uint16).  head_dim must be 64 or 128.  Query, key and value buffers
@@ -56,7 +60,10 @@ typedef enum skv_status {
   SKV_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query returns     */
   SKV_ERR_ALIGN = 6,     /* a pointer or the head stride is not 16-byte aligned  */
   SKV_ERR_ALIAS = 7,     /* outputs overlap inputs other than the in-place form  */
-  SKV_ERR_HIP = 8        /* a HIP runtime call or kernel launch failed           */
+  SKV_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed           */
+  SKV_ERR_INTERNAL = 9   /* host-side failure inside the library (a C++          */
+                         /* exception, e.g. out of host memory) caught at the    */
+                         /* interface; outputs are then unspecified              */
 } skv_status;
 
 typedef enum skv_dtype { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
@@ -245,7 +252,9 @@ skv_status speckv_decode_attention(const skv_shape* shape, int64_t n_rows, const
  * While enabled, every kernel the library launches is bracketed by a pair
  * of events on its stream.  speckv_profile_read synchronizes on the
  * recorded events and reports, per kernel name, the launch count and the
- * summed event time.  Process-wide state, not thread-safe; off by default. */
+ * summed event time.  Process-wide state, not thread-safe; off by default.
+ * If a sample could not be recorded (host memory exhausted), the read
+ * returns SKV_ERR_INTERNAL after filling in the totals it has. */
 skv_status speckv_profile_enable(int32_t on);
 int32_t speckv_profile_count(void);
 skv_status speckv_profile_read(int32_t index, const char** name, int64_t* launches, double* total_ms);

@@ -278,3 +278,61 @@ def test_empty_prefix_accepts_null_scores(lib):
     sp = shape()
     assert lib.speckv_scores(ctypes.byref(sp), q, k, None, ws, 1 << 30, None) == NULL
     assert lib.speckv_select(ctypes.byref(sp), None, 16, 1, 7, P(4 << 30), None, ws, 1 << 30, None) == NULL
+
+
+def test_specpc_workspace_suffices_for_every_l_skip(lib):
+    # Fewer used layers can give the planner more key chunks (larger pass-1
+    # partials): the size the query returns must hold for every l_skip.  A
+    # 4-byte-aligned workspace of exactly that size passes the size check and
+    # stops at the alignment check, before anything is launched.
+    for L, n_in, W in ((3, 65536, 1024), (5, 32768, 512), (24, 32768, 512), (2, 4096, 64)):
+        s = skv.make_shape(L, 2, 2, 64, n_in, W, 1, skv.SKV_BF16)
+        st, nbytes = _ws_bytes(lib, s, 0)
+        assert st == OK
+        for l_skip in range(L):
+            got = lib.specpc_token_scores(ctypes.byref(s), l_skip, P(1 << 30), P(2 << 30), None, P(3 << 30),
+                                          P((4 << 30) + 4), nbytes, None)
+            assert got == ALIGN, (L, n_in, W, l_skip, got)
+            short = lib.specpc_token_scores(ctypes.byref(s), l_skip, P(1 << 30), P(2 << 30), None, P(3 << 30),
+                                            P((4 << 30) + 4), 64, None)
+            assert short == WS
+
+
+def test_scores_rejects_overlapping_outputs(lib):
+    s = shape()  # q: 2 x 8 x 24 x 128 bf16 = 96 KiB; k: 2 x 2 x 1000 x 128 bf16 = 1000 KiB; scores 2 x 2 x 984 x 4
+    _, nbytes = _ws_bytes(lib, s)
+    q, k, sc, ws = 1 << 30, 2 << 30, 3 << 30, 4 << 30
+    f = lambda q_, k_, s_, w_: lib.speckv_scores(ctypes.byref(s), P(q_), P(k_), P(s_), P(w_), nbytes, None)
+    assert f(q, k, q + 4096, ws) == ALIAS          # scores inside Q
+    assert f(q, k, k + 512 * 1024, ws) == ALIAS    # scores inside K
+    assert f(q, k, sc, sc + 4096) == ALIAS         # workspace over the scores
+    assert f(q, k, sc, q + 1024) == ALIAS          # workspace over Q
+    assert f(q, k, sc, k + 16) == ALIAS            # workspace over K
+    fr = lambda rows, s_, w_: lib.speckv_scores_rows(ctypes.byref(s), P(q), P(k), P(rows), 1000, P(s_), P(w_),
+                                                      nbytes, None)
+    assert fr(sc + 64, sc, ws) == ALIAS            # row list inside the scores
+    assert fr(ws + 64, sc, ws) == ALIAS            # row list inside the workspace
+
+
+def test_select_rejects_overlapping_outputs(lib):
+    s = shape()  # scores and pooled 2 x 2 x 984 x 4 bytes; kept 2 x 2 x 80 x 4
+    sel = lambda sc, kept, pooled, ws: lib.speckv_select(ctypes.byref(s), P(sc), 64, 1, 7, P(kept), P(pooled),
+                                                         P(ws), 1 << 30, None)
+    sc, kept, pooled, ws = 1 << 30, 2 << 30, 3 << 30, 4 << 30
+    assert sel(sc, kept, kept + 64, ws) == ALIAS    # pooled over kept
+    # mean pooling without a pooled output uses the workspace for it
+    mean = lambda sc_, kept_, ws_: lib.speckv_select(ctypes.byref(s), P(sc_), 64, 2, 7, P(kept_), None, P(ws_),
+                                                     1 << 30, None)
+    assert mean(sc, kept, sc + 64) == ALIAS         # workspace over the scores
+    assert mean(sc, kept, kept - 64) == ALIAS       # workspace over kept
+
+
+def test_in_place_compact_rejects_kept_inside_staging(lib):
+    s = shape()
+    k, v, ws = 1 << 30, 2 << 30, 4 << 30
+    assert lib.speckv_compact(ctypes.byref(s), P(k), P(v), P(ws + 4096), 80, P(k), P(v), P(ws), 1 << 30,
+                              None) == ALIAS
+
+
+def test_internal_status_is_named(lib):
+    assert lib.speckv_status_string(9) == b"host-side failure inside the library"
