@@ -53,16 +53,25 @@ skv_status check_shape(const skv_shape* s, Dims* d) {
   d->D = s->head_dim;
   d->n_in = s->n_in;
   d->esize = (s->dtype == SKV_F32) ? 4 : 2;
+  // unit counts must stay inside int32 for the kernels
+  if (d->L * d->Hq > INT32_MAX / 2) return SKV_ERR_SHAPE;
   d->stride = s->kv_head_stride ? s->kv_head_stride : s->n_in * s->head_dim;
   if (d->stride < d->n_in * d->D) return SKV_ERR_SHAPE;
+  // Every size the library forms (buffer spans, workspace pieces) stays far
+  // inside int64: the K/V span below 2^60 bytes, L * Hq * n_in below 2^56 and
+  // the query rows L * Hq * (n_window + n_lookahead) below 2^40.
+  constexpr int64_t kSpan = INT64_C(1) << 60;
+  if (d->stride > kSpan / (d->L * d->Hkv * d->esize)) return SKV_ERR_SHAPE;
+  if (d->n_in > (INT64_C(1) << 56) / (d->L * d->Hq)) return SKV_ERR_SHAPE;
+  if ((int64_t)s->n_window + s->n_lookahead > (INT64_C(1) << 40) / (d->L * d->Hq)) return SKV_ERR_SHAPE;
   if ((d->stride * d->esize) % 16 != 0) return SKV_ERR_ALIGN;
   d->n_window = s->n_window;
   d->n_lookahead = s->n_lookahead;
   d->scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->head_dim));
   d->dtype = s->dtype;
   const int64_t G = d->Hq / d->Hkv;
-  // row counts and unit counts must stay inside int32 for the kernels
-  if (G * (d->n_window + d->n_lookahead) > INT32_MAX / 2 || d->L * d->Hq > INT32_MAX / 2) return SKV_ERR_SHAPE;
+  // query rows per unit must stay inside int32 for the kernels
+  if (G * (d->n_window + d->n_lookahead) > INT32_MAX / 2) return SKV_ERR_SHAPE;
   return SKV_OK;
 }
 
@@ -138,9 +147,17 @@ PcWs specpc_ws(const Dims& d, int64_t units) {
 // Workspace of specpc_token_scores for any l_skip: the planner may give fewer
 // units (a larger l_skip) more key chunks, hence larger pass-1 partials, so
 // the size is the maximum over every l_skip in [0, L).
+//
+// The planner gives a unit more than one key chunk only while the launch has
+// fewer blocks than its target; past that the plan of a unit no longer
+// depends on the unit count and the workspace grows with it, so l_skip = 0
+// is the largest of those.  Only the l_skip values with fewer units than a
+// few times the target need a look.
 size_t specpc_ws_any_lskip(const Dims& d) {
-  size_t need = 0;
-  for (int64_t ls = 0; ls < d.L; ++ls) need = std::max(need, specpc_ws(d, (d.L - ls) * d.Hkv).end);
+  const int64_t few = 4 * score_plan_target_blocks();
+  size_t need = specpc_ws(d, d.L * d.Hkv).end;
+  for (int64_t ls = std::max<int64_t>(1, d.L - few / d.Hkv - 1); ls < d.L; ++ls)
+    need = std::max(need, specpc_ws(d, (d.L - ls) * d.Hkv).end);
   return need;
 }
 
@@ -273,7 +290,7 @@ size_t kv_span(const Dims& d, int64_t rows_last) {
 
 extern "C" {
 
-const char* speckv_status_string(skv_status status) {
+const char* speckv_status_string(int32_t status) {
   switch (status) {
     case SKV_OK: return "ok";
     case SKV_ERR_NULL: return "required pointer is NULL";

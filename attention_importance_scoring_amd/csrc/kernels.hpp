@@ -46,6 +46,7 @@ struct ScorePlan {
   size_t lds_pass1, lds_pass2;  // dynamic LDS bytes per block
 };
 void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl);
+int64_t score_plan_target_blocks();  // blocks per launch the planner aims at
 hipError_t launch_score_pass1(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s);
 hipError_t launch_lse_combine(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_pass2(int dtype, int head_dim, int kt, const ScoreArgs& a, size_t lds, hipStream_t s);

@@ -559,6 +559,8 @@ static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan
   }
 }
 
+int64_t score_plan_target_blocks() { return SKV_TARGET_BLOCKS; }
+
 void score_plan(int dtype, int head_dim, int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   if (dtype == 0) {
     if (head_dim == 64) plan_pick<float, 64>(n_units, n_rows, n_keys, pl);

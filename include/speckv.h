@@ -103,7 +103,7 @@ typedef struct skv_shape {
 } skv_shape;
 
 /* Human-readable name of a status code (static storage). */
-const char* speckv_status_string(skv_status status);
+const char* speckv_status_string(int32_t status); /* any value; unknown codes get "unknown status" */
 
 /* Workspace bytes that suffice for every entry point below on this shape
  * (SpecKV with the given C_max, or SpecPC when called as such).  The same
