@@ -174,8 +174,12 @@ def _heavy_hitter_positions(kind: str, n_in: int, n_pre: int, g, device) -> torc
     raise ValueError(kind)
 
 
-def speckv_layer(cfg: SpecKVConfig, layer: int, seed: int, device="cpu"):
-    """One layer of inputs: q_obs [Hq, n_obs, d], k [Hkv, n_in, d], v [Hkv, n_in, d]."""
+def speckv_layer(cfg: SpecKVConfig, layer: int, seed: int, device="cpu", planted=None):
+    """One layer of inputs: q_obs [Hq, n_obs, d], k [Hkv, n_in, d], v [Hkv, n_in, d].
+
+    planted: None, or a list to which the positions of the planted keys
+    (heavy hitters and the sink at 0) of each KV head are appended (the
+    positions themselves, not anything computed from them)."""
     d, Hq, Hkv, G = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.G
     q = _randn((Hq, cfg.n_obs, d), _gen(seed, layer, "q", device), device)
     k = _randn((Hkv, cfg.n_in, d), _gen(seed, layer, "k", device), device)
@@ -200,6 +204,8 @@ def speckv_layer(cfg: SpecKVConfig, layer: int, seed: int, device="cpu"):
             pos = _heavy_hitter_positions(cfg.heavy_hitters, cfg.n_in, cfg.n_pre, gh, device)
             pos = torch.cat([torch.zeros(1, dtype=pos.dtype, device=device), pos])
             k[h, pos] = cfg.beta * math.sqrt(d) * u[h] + _randn((pos.numel(), d), gh, device)
+            if planted is not None:
+                planted.append(pos.cpu())
     v = _randn((Hkv, cfg.n_in, d), _gen(seed, layer, "v", device), device)
     dt = cfg.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)
@@ -210,7 +216,9 @@ def speckv_inputs(cfg: SpecKVConfig, seed: int, device="cpu", layers=None, kv_he
 
     Returns dict with q_obs [L, Hq, n_obs, d], k and v as [L, Hkv, n_in, d]
     views (when kv_head_stride is given, k and v are views of a larger
-    buffer whose head slabs are kv_head_stride elements apart).
+    buffer whose head slabs are kv_head_stride elements apart), and
+    "planted": per layer, per KV head, the planted key positions (empty lists
+    when the workload plants none).
     """
     layers = list(range(cfg.n_layers)) if layers is None else list(layers)
     L, d = len(layers), cfg.head_dim
@@ -220,14 +228,18 @@ def speckv_inputs(cfg: SpecKVConfig, seed: int, device="cpu", layers=None, kv_he
     q_obs = torch.empty((L, cfg.n_q_heads, cfg.n_obs, d), dtype=dt, device=device)
     kbuf = torch.empty((L, cfg.n_kv_heads, stride), dtype=dt, device=device)
     vbuf = torch.empty((L, cfg.n_kv_heads, stride), dtype=dt, device=device)
+    planted = []
     for i, layer in enumerate(layers):
-        q, k, v = speckv_layer(cfg, layer, seed, device)
+        pl = []
+        q, k, v = speckv_layer(cfg, layer, seed, device, planted=pl)
+        planted.append(pl)
         q_obs[i] = q
         kbuf[i, :, :cfg.n_in * d] = k.reshape(cfg.n_kv_heads, -1)
         vbuf[i, :, :cfg.n_in * d] = v.reshape(cfg.n_kv_heads, -1)
     k_view = kbuf[:, :, :cfg.n_in * d].unflatten(2, (cfg.n_in, d))
     v_view = vbuf[:, :, :cfg.n_in * d].unflatten(2, (cfg.n_in, d))
-    return {"q_obs": q_obs, "k": k_view, "v": v_view, "k_buf": kbuf, "v_buf": vbuf, "kv_head_stride": stride}
+    return {"q_obs": q_obs, "k": k_view, "v": v_view, "k_buf": kbuf, "v_buf": vbuf, "kv_head_stride": stride,
+            "planted": planted}
 
 
 def specpc_layer(cfg: SpecPCConfig, layer: int, seed: int, device="cpu"):

@@ -18,6 +18,7 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 """
 from .speckv import (  # noqa: F401
     default_scale,
+    row_logits,
     row_probabilities,
     head_scores,
     speckv_scores,

@@ -34,19 +34,26 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def row_logits(q_rows, k_prefix, scale: float) -> np.ndarray:
+    """Pre-softmax scores s_rj = scale * <q_r, k_j> of the observation rows
+    q_rows [R, d] against the keys k_prefix [n, d]; returns [R, n].
+
+    Reading: the usual scaled dot product, the scale applied after the
+    product (the pages do not print the score formula)."""
+    return scale * (_as_f64(q_rows) @ _as_f64(k_prefix).T)
+
+
 def row_probabilities(q_rows, k_prefix, scale: float) -> np.ndarray:
     """Softmax of each observation query row over the remaining input keys.
 
     q_rows: [R, d]; k_prefix: [n_pre, d]. Returns P [R, n_pre] with
-    P[r, j] = exp(s_rj - lse_r), s_rj = scale * <q_r, k_j>,
+    P[r, j] = exp(s_rj - lse_r), s_rj = row_logits (scale * <q_r, k_j>),
     lse_r = m_r + log(sum_j exp(s_rj - m_r)), m_r = max_j s_rj.
 
     Reading: the normaliser of each row is the set of remaining input keys
     only (the keys that are scored), so every row sums to one over them.
     """
-    q = _as_f64(q_rows)
-    k = _as_f64(k_prefix)
-    s = scale * (q @ k.T)
+    s = row_logits(q_rows, k_prefix, scale)
     m = s.max(axis=1, keepdims=True)
     lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
     return np.exp(s - lse)

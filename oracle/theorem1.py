@@ -15,10 +15,13 @@ from __future__ import annotations
 
 import numpy as np
 
+from .speckv import row_logits
+
 
 def pre_softmax_scores(q, k, scale: float = 1.0) -> np.ndarray:
-    """s_j = scale * <q, k_j> for one query q [d] against keys k [n, d]."""
-    return scale * (np.asarray(k, dtype=np.float64) @ np.asarray(q, dtype=np.float64))
+    """s_j = scale * <q, k_j> for one query q [d] against keys k [n, d]: the
+    logits the SpecKV scoring itself feeds to its softmax (row_logits)."""
+    return row_logits(np.asarray(q, dtype=np.float64)[None, :], k, scale)[0]
 
 
 def theorem1_bound(eps: float, w_q, w_k, x_keys=None) -> float:

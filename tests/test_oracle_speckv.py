@@ -247,3 +247,27 @@ def test_bruteforce_max_and_per_query_head_tiny(seed):
                     want_pqh[l, hq, j] += p
     np.testing.assert_allclose(oracle.speckv_scores(q, k, n_window, aggregation="max"), want_max, rtol=1e-12)
     np.testing.assert_allclose(oracle.speckv_scores(q, k, n_window, per_query_head=True), want_pqh, rtol=1e-12)
+
+
+def test_planted_heavy_hitters_recovered_qwen32b_shape_64k():
+    # The 64K Qwen2.5-32B-shaped workload (rank-8 keys plus 1 % planted heavy
+    # hitters and the sink), two layers in fp64: every kept prefix key lies
+    # within the pooling half-width of a planted key.  The 656 planted keys
+    # per head make about 4600 plateau slots against C_max = 256, so only the
+    # strongest fit: the kept keys form 256 / 7 (about 37) whole plateaus.
+    import numpy as np
+    from attention_importance_scoring_amd import workloads as w
+    cfg = w.QWEN32B_64K
+    inp = w.speckv_inputs(cfg, seed=3, layers=[0, 63])
+    s = oracle.speckv_scores(w.to_numpy_f64(inp["q_obs"]), w.to_numpy_f64(inp["k"]), cfg.n_window)
+    kept, _ = oracle.speckv_select(s, cfg.C_max, cfg.n_window, "max", cfg.pool_kernel)
+    r = cfg.pool_kernel // 2
+    for i in range(2):
+        for h in range(cfg.n_kv_heads):
+            planted = inp["planted"][i][h].numpy()
+            assert len(planted) == cfg.n_in // 100 + 1 and planted[0] == 0
+            prefix = kept[i, h, :cfg.C_max]
+            dist = np.abs(prefix[:, None] - planted[None, :]).min(axis=1)
+            assert (dist <= r).all(), f"layer {i} head {h}: kept keys far from every planted key"
+            near = np.abs(planted[:, None] - prefix[None, :]).min(axis=1) == 0
+            assert near.sum() >= cfg.C_max // cfg.pool_kernel, "too few planted keys kept"

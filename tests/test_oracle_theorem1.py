@@ -2,8 +2,9 @@
 section "Key designs", SpecKV: ||s - s_hat||_2 <= eps ||W_q W_k^T||_2 on the
 pre-softmax scores when the query embedding is perturbed by at most eps).
 
-The scores are computed with the oracle's own score function; key embeddings
-X have orthonormal rows, so ||X||_2 = 1 and the printed form applies.
+The scores are the logits of the oracle's own SpecKV scoring (row_logits,
+the input of its softmax); key embeddings X have orthonormal rows, so
+||X||_2 = 1 and the printed form applies.
 """
 import numpy as np
 import pytest
@@ -54,3 +55,20 @@ def test_scale_enters_linearly():
     s1 = oracle.pre_softmax_scores(x @ w_q, X @ w_k, 1.0)
     s2 = oracle.pre_softmax_scores(x @ w_q, X @ w_k, 0.125)
     np.testing.assert_allclose(s2, 0.125 * s1, rtol=1e-15)
+
+
+def test_bound_holds_on_the_logits_the_scoring_softmax_uses():
+    # the same perturbation seen through row_probabilities: its log-probabilities
+    # are the logits up to a per-row constant, so the centred log-probabilities
+    # move by at most the bound too (centring is an orthogonal projection)
+    import scipy.special
+    rng, w_q, w_k, _, X, x = _setup(7)
+    K = X @ w_k
+    p = oracle.row_probabilities((x @ w_q)[None], K, 1.0)[0]
+    np.testing.assert_allclose(p, scipy.special.softmax(oracle.pre_softmax_scores(x @ w_q, K)), rtol=1e-13)
+    for eps in (1e-3, 0.1, 1.0):
+        e = rng.standard_normal(x.shape)
+        e *= eps / np.linalg.norm(e)
+        p_hat = oracle.row_probabilities(((x + e) @ w_q)[None], K, 1.0)[0]
+        d = np.log(p) - np.log(p_hat)
+        assert np.linalg.norm(d - d.mean()) <= oracle.theorem1_bound(eps, w_q, w_k) * (1 + 1e-10)
