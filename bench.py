@@ -59,157 +59,224 @@ def parse():
     return p.parse_args()
 
 
-def cpu_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
-        pass
-    return len(os.sched_getaffinity(0))
-
-
-def speckv_cpu_baseline(cfg, inp, budget_s=12.0):
-    """The fp64 oracle (scores, pooling, selection, compaction) on whole
-    (layer, KV head) units of the same workload, until ~budget_s of work."""
+def _raw(t):
+    """Host copy of a tensor's raw elements: bfloat16 as its uint16 words, float32 as is."""
     import numpy as np
     import torch
-    import oracle
-    from attention_importance_scoring_amd import workloads as wl
-    G = cfg.G
-    done, keys, t_total = 0, 0, 0.0
-    L = inp["q_obs"].shape[0]
-    units = [(l, h) for l in range(L) for h in range(cfg.n_kv_heads)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(units))
-    for idx in order:
-        l, h = units[idx]
-        q = wl.to_numpy_f64(inp["q_obs"][l, h * G:(h + 1) * G])
-        k = wl.to_numpy_f64(inp["k"][l, h])
-        v = inp["v"][l, h].cpu()
-        v_raw = v.view(torch.int16).numpy() if v.dtype == torch.bfloat16 else v.numpy()  # bit copy
+    t = t.detach().contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _single_core(fn):
+    """Seconds of fn() in this process with one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        s = oracle.head_scores(q, k[:cfg.n_pre], oracle.default_scale(cfg.head_dim))
-        pooled = oracle.pool1d(s, cfg.pool_kernel, "max")
-        kept = oracle.select_kept(pooled, cfg.C_max, cfg.n_window)
-        oracle.compact_rows(k, kept)
-        oracle.compact_rows(v_raw, kept)
-        t_total += time.perf_counter() - t0
-        done += 1
-        keys += cfg.n_in
-        if t_total >= budget_s:
-            break
-    return {"value": keys / t_total, "unit": "keys/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{done} of {len(units)} (layer, KV head) units of the same workload, {keys} keys, "
-                      f"{t_total:.1f} s of fp64 NumPy"}
+        fn()
+        return time.perf_counter() - t0
 
 
-def decode_cpu_baseline(cfg, inp, cache, budget_s=10.0):
-    """The fp64 decode-attention oracle on whole (layer, KV head) units of
-    the same caches (the compacted 288-row one unless only the full cache is
-    benchmarked), until ~budget_s of work; scaled to all-layer decode steps/s."""
+def speckv_cpu_baseline(cfg, inp, budget_s=10.0):
+    """The fp64 oracle (scores, pooling, selection, compaction of K and V) on
+    whole (layer, KV head) units of the same workload, in a pool of one
+    single-threaded worker per core (at most 16); the sample is sized from a
+    single-core timing of one unit to about budget_s of wall time.  Also
+    reports that single-core time scaled to every unit (extrapolated)."""
     import numpy as np
     import oracle
-    from attention_importance_scoring_amd import workloads as wl
+    from oracle.pool import OraclePool, exact_f64, worker_count
+    G, L, H = cfg.G, inp["q_obs"].shape[0], cfg.n_kv_heads
+    units = [(l, h) for l in range(L) for h in range(H)]
+    order = np.random.default_rng(0).permutation(len(units))
+    scale = oracle.default_scale(cfg.head_dim)
+
+    def task(i):
+        l, h = units[order[i]]
+        return dict(uid=i, q=_raw(inp["q_obs"][l, h * G:(h + 1) * G]), k=_raw(inp["k"][l, h]),
+                    v=_raw(inp["v"][l, h]), n_pre=cfg.n_pre, scale=scale, step=True, pool_kernel=cfg.pool_kernel,
+                    C_max=cfg.C_max, n_window=cfg.n_window)
+
+    t0 = task(0)
+
+    def one_unit():
+        s = oracle.head_scores(exact_f64(t0["q"]), exact_f64(t0["k"])[:cfg.n_pre], scale)
+        kept = oracle.select_kept(oracle.pool1d(s, cfg.pool_kernel, "max"), cfg.C_max, cfg.n_window)
+        oracle.compact_rows(t0["k"], kept)
+        oracle.compact_rows(t0["v"], kept)
+
+    t1 = _single_core(one_unit)
+    n = worker_count()
+    n_units = int(min(len(units), max(n, round(budget_s * n / t1))))
+    with OraclePool(n) as pool:
+        w0 = time.perf_counter()
+        busy = sum(sec for _, _, sec in pool.imap("speckv", (task(i) for i in range(n_units))))
+        wall = time.perf_counter() - w0
+    step_1core = t1 * len(units)
+    return {"value": n_units * cfg.n_in / wall, "unit": "keys/s", "cores": n, "kind": "oracle",
+            "sample": f"{n_units} of {len(units)} (layer, KV head) units of the same workload ({n_units * cfg.n_in} "
+                      f"keys: fp64 scores, max-pool, selection, K/V compaction) on a pool of {n} single-threaded "
+                      f"worker processes ({len(os.sched_getaffinity(0))} cores in the affinity mask): {wall:.1f} s "
+                      f"wall, {busy:.1f} s in the workers",
+            "single_core_extrapolated": {"unit_s": round(t1, 3), "units": len(units), "step_s": round(step_1core, 1),
+                                         "value": len(units) * cfg.n_in / step_1core, "unit": "keys/s",
+                                         "note": "one unit timed on one core with one BLAS thread, scaled to "
+                                                 "every unit of the step"}}
+
+
+def decode_cpu_baseline(cfg, inp, cache, budget_s=8.0):
+    """The fp64 decode-attention oracle on whole (layer, KV head) units of
+    the same caches (the compacted 288-row one unless only the full cache is
+    benchmarked) in a pool of single-threaded workers, scaled to all-layer
+    decode steps/s; plus one unit on one core, extrapolated."""
+    import numpy as np
+    import oracle
+    from oracle.pool import OraclePool, exact_f64, worker_count
     G, d = cfg.G, cfg.head_dim
     L, H = cfg.n_layers, cfg.n_kv_heads
     n_rows = cfg.n_keep if cache != "full" else cfg.n_in
     rng = np.random.default_rng(0)
-    q = rng.standard_normal((1, G, d))
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    scale = oracle.default_scale(d)
     order = rng.permutation(L * H)
-    units = []  # host copies of up to 64 units, visited round-robin until the budget is spent
-    for idx in order[:64]:
-        layer, h = divmod(int(idx), H)
-        units.append((wl.to_numpy_f64(inp["k"][layer:layer + 1, h:h + 1, :n_rows]),
-                      wl.to_numpy_f64(inp["v"][layer:layer + 1, h:h + 1, :n_rows])))
-    done, t_total = 0, 0.0
-    while t_total < budget_s:
-        k, v = units[done % len(units)]
-        t0 = time.perf_counter()
-        oracle.decode_attention(q, k, v)
-        t_total += time.perf_counter() - t0
-        done += 1
-    per_step = t_total / done * (L * H)
-    return {"value": 1.0 / per_step, "unit": "decode steps/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{done} unit decodes over {len(units)} distinct (layer, KV head) units of {n_rows} rows "
-                      f"(the first rows of the full cache stand in for the compacted ones), {t_total:.1f} s of "
-                      f"fp64 NumPy, scaled to all {L * H} units of one decode step"}
+    raw = [(q, _raw(inp["k"][i // H, i % H, :n_rows]), _raw(inp["v"][i // H, i % H, :n_rows])) for i in order[:64]]
+    t1 = _single_core(lambda: oracle.head_attention(exact_f64(raw[0][0]), exact_f64(raw[0][1]),
+                                                    exact_f64(raw[0][2]), scale))
+    n = worker_count()
+    per_task = max(1, int(0.2 / max(t1, 1e-6)))  # about 0.2 s of work per task
+    n_tasks = max(n, int(budget_s * n / (per_task * t1)))
+    tasks = (dict(uid=i, scale=scale, units=[raw[(i * per_task + j) % len(raw)] for j in range(per_task)])
+             for i in range(n_tasks))
+    with OraclePool(n) as pool:
+        w0 = time.perf_counter()
+        for _ in pool.imap("decode", tasks):
+            pass
+        wall = time.perf_counter() - w0
+    done = n_tasks * per_task
+    return {"value": done / (L * H) / wall, "unit": "decode steps/s", "cores": n, "kind": "oracle",
+            "sample": f"{done} unit decodes over {len(raw)} distinct (layer, KV head) units of {n_rows} rows (the "
+                      f"first rows of the full cache stand in for the compacted ones) on a pool of {n} "
+                      f"single-threaded workers, {wall:.1f} s wall, scaled to all {L * H} units of one decode step",
+            "single_core_extrapolated": {"unit_s": t1, "value": 1.0 / (t1 * L * H), "unit": "decode steps/s",
+                                         "note": "one unit timed on one core, scaled to every unit of the step"}}
 
 
-def _specpc_oracle_time(cfg, inp, budget_s):
-    """Seconds per step of the fp64 oracle's SpecPC token scores and selection:
-    one used layer at a time (all its query heads) until ~budget_s, scaled
-    to every used layer.  Returns (seconds, layers timed, used layers,
-    selection seconds, kept tokens)."""
-    import oracle
-    from attention_importance_scoring_amd import workloads as wl
-    used = list(range(cfg.l_skip, cfg.n_layers))
-    done, t_layers, scores = 0, 0.0, None
-    for layer in used:
-        q = wl.to_numpy_f64(inp["q_win"][layer:layer + 1])
-        k = wl.to_numpy_f64(inp["k"][layer:layer + 1])
-        t0 = time.perf_counter()
-        scores = oracle.specpc_token_scores(q, k, 0, n_in=cfg.n_in)
-        t_layers += time.perf_counter() - t0
-        done += 1
-        if t_layers >= budget_s:
-            break
-    t0 = time.perf_counter()
-    tokens, _ = oracle.specpc_select(scores, cfg.k_top, "max", cfg.pool_kernel)
-    t_sel = time.perf_counter() - t0
-    return t_layers / done * len(used) + t_sel, done, len(used), t_sel, tokens
-
-
-def specpc_cpu_baseline(cfg, inp, budget_s=12.0):
-    """The fp64 oracle's SpecPC token scores one used layer at a time (all
-    its query heads), until ~budget_s of work, scaled to every used layer,
-    plus its pooling and selection once."""
-    per_step, done, n_used, t_sel, _ = _specpc_oracle_time(cfg, inp, budget_s)
-    return {"value": cfg.n_in / per_step, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{done} of {n_used} used layers ({done * cfg.n_q_heads} causal window maps of "
-                      f"{cfg.window} x {cfg.n_keys}), about {budget_s:.0f} s of fp64 NumPy, scaled to all used "
-                      f"layers, plus pooling and selection ({t_sel:.2f} s)"}
-
-
-def cascade_cpu_baseline(cc, inp, budget_s=12.0):
-    """The fp64 oracle's cascade: SpecPC on the draft as in
-    specpc_cpu_baseline (half the budget), then SpecKV on the compressed
-    prompt over whole (layer, KV head) units of the target, gathering the
-    kept tokens' rows, scoring, pooling, selecting and compacting (the
-    other half), scaled to all units."""
+def _specpc_oracle_pool(cfg, inp, n):
+    """The fp64 oracle's SpecPC token scores over every used (layer, query
+    head) map, the maps split in batches over a pool of n single-threaded
+    workers (each returns the sum of its maps), then the mean, the weighted
+    max, pooling and selection in this process.  Returns (wall seconds,
+    kept tokens, single-core seconds of one map, maps)."""
     import numpy as np
-    import torch
     import oracle
-    from attention_importance_scoring_amd import workloads as wl
+    from oracle.pool import OraclePool, exact_f64
+    used = range(cfg.l_skip, cfg.n_layers)
+    G = cfg.G
+    maps = [(l, hq) for l in used for hq in range(cfg.n_q_heads)]
+    scale = oracle.default_scale(cfg.head_dim)
+    k_raw = {(l, h): _raw(inp["k"][l, h]) for l in used for h in range(cfg.n_kv_heads)}
+    q_raw = {(l, hq): _raw(inp["q_win"][l, hq]) for l, hq in maps}
+    l0, h0 = maps[0]
+    t1 = _single_core(lambda: oracle.causal_window_probabilities(exact_f64(q_raw[l0, h0]),
+                                                                  exact_f64(k_raw[l0, h0 // G]), scale))
+    batches = np.array_split(np.arange(len(maps)), 2 * n)
+    tasks = (dict(uid=i, scale=scale, n_in=cfg.n_in,
+                  maps=[(q_raw[maps[m]], k_raw[maps[m][0], maps[m][1] // G]) for m in b])
+             for i, b in enumerate(batches) if len(b))
+    with OraclePool(n) as pool:
+        w0 = time.perf_counter()
+        acc = None
+        for _, part, _ in pool.imap("specpc_maps", tasks):
+            acc = part if acc is None else acc + part
+        abar = acc / len(maps)
+        w = oracle.default_query_weights(cfg.window)
+        scores = (w[:, None] * abar).max(axis=0)
+        tokens, _ = oracle.specpc_select(scores, cfg.k_top, "max", cfg.pool_kernel)
+        wall = time.perf_counter() - w0
+    return wall, tokens, t1, len(maps)
+
+
+def specpc_cpu_baseline(cfg, inp):
+    """The fp64 oracle's SpecPC token scores and selection over the whole
+    draft stack on a pool of single-threaded workers; plus one map on one
+    core scaled to every map (extrapolated)."""
+    from oracle.pool import worker_count
+    n = worker_count()
+    wall, _, t1, n_maps = _specpc_oracle_pool(cfg, inp, n)
+    return {"value": cfg.n_in / wall, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"the whole step: {n_maps} causal window maps of {cfg.window} x {cfg.n_keys} over a pool of {n} "
+                      f"single-threaded workers, then mean, weighted max, pooling and selection: {wall:.1f} s wall",
+            "single_core_extrapolated": {"map_s": round(t1, 3), "maps": n_maps, "step_s": round(t1 * n_maps, 1),
+                                         "value": cfg.n_in / (t1 * n_maps), "unit": "tokens/s",
+                                         "note": "one map timed on one core, scaled to every map"}}
+
+
+def cascade_cpu_baseline(cc, inp):
+    """The fp64 oracle's cascade: SpecPC on the draft as in
+    specpc_cpu_baseline, then SpecKV on the compressed prompt over every
+    (layer, KV head) unit of the target (gather of the kept tokens' rows,
+    scores, pooling, selection, compaction), both on the same pool size."""
+    import numpy as np
+    import oracle
+    from oracle.pool import OraclePool, worker_count
     dr, tg = cc.draft, cc.target
-    pc_s, pc_done, pc_used, _, tokens = _specpc_oracle_time(dr, inp["draft"], budget_s / 2)
+    n = worker_count()
+    pc_wall, tokens, _, _ = _specpc_oracle_pool(dr, inp["draft"], n)
     t_in = inp["target"]
     G, n_tok = tg.n_q_heads // tg.n_kv_heads, len(tokens)
+    scale = oracle.default_scale(tg.head_dim)
     units = [(l, h) for l in range(tg.n_layers) for h in range(tg.n_kv_heads)]
-    order = np.random.default_rng(0).permutation(len(units))
-    done, t_units = 0, 0.0
-    for idx in order:
-        l, h = units[idx]
-        q = wl.to_numpy_f64(t_in["q_obs"][l, h * G:(h + 1) * G])
-        k = wl.to_numpy_f64(t_in["k"][l, h])
-        v = t_in["v"][l, h].cpu()
-        v_raw = v.view(torch.int16).numpy() if v.dtype == torch.bfloat16 else v.numpy()  # bit copy
-        t0 = time.perf_counter()
-        k_c, v_c = k[tokens], v_raw[tokens]
-        s = oracle.head_scores(q, k_c[:n_tok - tg.n_window], oracle.default_scale(tg.head_dim))
-        kept = oracle.select_kept(oracle.pool1d(s, tg.pool_kernel, "max"), tg.C_max, tg.n_window)
-        oracle.compact_rows(k_c, kept)
-        oracle.compact_rows(v_c, kept)
-        t_units += time.perf_counter() - t0
-        done += 1
-        if t_units >= budget_s / 2:
-            break
-    per_step = pc_s + t_units / done * len(units)
-    return {"value": dr.n_in / per_step, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"SpecPC: {pc_done} of {pc_used} used draft layers, scaled to all; SpecKV on the "
-                      f"{n_tok}-token prompt: {done} of {len(units)} (layer, KV head) units, scaled to all; "
-                      f"about {budget_s:.0f} s of fp64 NumPy in total"}
+    tok = np.asarray(tokens)
+    w0 = time.perf_counter()
+    tasks = (dict(uid=i, q=_raw(t_in["q_obs"][l, h * G:(h + 1) * G]), k=_raw(t_in["k"][l, h])[tok],
+                  v=_raw(t_in["v"][l, h])[tok], n_pre=n_tok - tg.n_window, scale=scale, step=True,
+                  pool_kernel=tg.pool_kernel, C_max=tg.C_max, n_window=tg.n_window)
+             for i, (l, h) in enumerate(units))
+    with OraclePool(n) as pool:
+        for _ in pool.imap("speckv", tasks):
+            pass
+    kv_wall = time.perf_counter() - w0
+    return {"value": dr.n_in / (pc_wall + kv_wall), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"the whole cascade on a pool of {n} single-threaded workers: SpecPC over the draft stack "
+                      f"{pc_wall:.1f} s, SpecKV over all {len(units)} (layer, KV head) units of the {n_tok}-token "
+                      f"prompt {kv_wall:.1f} s (wall)"}
+
+
+def timed_steps(step, steps, stream, torch):
+    """Runs `steps` steps on `stream` between events: returns (mean ms over
+    the bracketed region, per-step ms from an event after every step)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
+def step_stats(per):
+    import statistics
+    return {"ms_per_step_median": round(statistics.median(per), 4), "ms_per_step_min": round(min(per), 4)}
+
+
+def input_digests(tensors):
+    """sha256 of the raw bytes of every (layer, tensor) of the inputs (layer =
+    first axis), and per tensor the sha256 of its layer digests in layer order.
+    Returns ({tensor: combined hex digest}, {tensor: [layer hex digests]})."""
+    import concurrent.futures
+    import hashlib
+    import torch
+
+    def layer_digest(t):
+        return hashlib.sha256(t.detach().contiguous().cpu().view(torch.uint8).numpy().tobytes()).hexdigest()
+
+    combined, per_layer = {}, {}
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        for name, t in tensors.items():
+            per_layer[name] = list(ex.map(layer_digest, [t[i] for i in range(t.shape[0])]))
+            combined[name] = hashlib.sha256("".join(per_layer[name]).encode()).hexdigest()
+    return combined, per_layer
 
 
 def traffic_for(kernel: str, workload: str, summary: str):
@@ -242,6 +309,11 @@ def bench_speckv(args, cfg, torch, skv, wl):
     inp = wl.speckv_inputs(cfg, seed=args.seed or 3, device=dev, layers=from_layers)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
+    # digests of the inputs as generated (the in-place workload overwrites its K/V during the steps)
+    combined, per_layer = input_digests({"q_obs": inp["q_obs"], "k": inp["k"], "v": inp["v"]})
+    print("[bench] input sha256 per layer: " + json.dumps(per_layer), file=sys.stderr, flush=True)
+    digests = {"scheme": "sha256 of the raw bytes of each (layer, tensor); per tensor, sha256 of its layer digests "
+                         "(hex, in layer order) concatenated", **combined}
     L, Hkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     H = cfg.n_q_heads if args.per_query_head else Hkv  # heads that get their own kept set
     dt = skv.SKV_F32 if cfg.dtype == "f32" else skv.SKV_BF16
@@ -281,14 +353,7 @@ def bench_speckv(args, cfg, torch, skv, wl):
         step()
     torch.cuda.synchronize()
     skv.profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
     skv.profile_enable(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
@@ -305,22 +370,28 @@ def bench_speckv(args, cfg, torch, skv, wl):
     avg_s = kern[dom]["avg_ms"] * 1e-3
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = flops_per_launch / avg_s / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+    roof = {"kernel": dom, "scope": "one launch of the dominant kernel (not the whole step; see path_mfma)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name, f"speckv_kernels_{cfg.name}_traffic.json") if default_variant else None}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
     path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
+    path = {"scope": "the whole step (scores + select + compact), one Q_obs K^T of algorithmic flops",
+            "frac": round(path_frac, 4), "target_frac": 0.40,
+            "ms_at_target": round(flops_per_pass / (0.40 * peak * 1e12) * 1e3, 3), "ms_measured": round(ms, 4)}
     out = {
         "metric": METRIC, "value": keys / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), **step_stats(per_step), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "n_layers": L, "n_q_heads": cfg.n_q_heads, "n_kv_heads": Hkv, "head_dim": d,
                    "n_in": cfg.n_in, "n_window": cfg.n_window, "n_lookahead": cfg.n_lookahead, "C_max": cfg.C_max,
                    "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys,
                    "aggregation": args.aggregation, "per_query_head": bool(args.per_query_head)},
         "roofline": roof,
         "path_mfma_frac": round(path_frac, 4),
+        "path_mfma": path,
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "ms_per_step": round(v["ms_per_step"], 4)}
                     for k, v in kern.items()},
+        "input_sha256": digests,
     }
     return out, inp
 
@@ -348,13 +419,7 @@ def bench_specpc(args, cfg, torch, skv, wl):
         step()
     torch.cuda.synchronize()
     skv.profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
     skv.profile_enable(False)
     kern = {name: {"avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
@@ -372,7 +437,8 @@ def bench_specpc(args, cfg, torch, skv, wl):
     return {
         "metric": "SpecPC tokens scored+selected/sec (draft attention stack)", "value": cfg.n_in / (ms * 1e-3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        **step_stats(per_step), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "l_skip": cfg.l_skip, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "n_in": cfg.n_in, "window": cfg.window,
                    "n_lookahead": cfg.n_lookahead, "k_top": cfg.k_top},
@@ -438,13 +504,7 @@ def bench_cascade(args, cc, torch, skv, wl):
         step()
     torch.cuda.synchronize()
     skv.profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
     skv.profile_enable(False)
     kern = {name: {"launches": n, "avg_ms": round(t / max(n, 1), 4), "ms_per_step": round(t / args.steps, 4)}
@@ -463,7 +523,8 @@ def bench_cascade(args, cc, torch, skv, wl):
     return {
         "metric": "SpecKV-PC cascade: prompt tokens compressed/sec (SpecPC to k_top tokens, SpecKV to C_max pairs)",
         "value": dr.n_in / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), **step_stats(per_step), "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": dr.dtype, "data": "synthetic",
         "config": {"workload": cc.name, "n_in": dr.n_in, "draft_layers": dr.n_layers, "l_skip": dr.l_skip,
                    "draft_heads": [dr.n_q_heads, dr.n_kv_heads, dr.head_dim], "window": dr.window, "k_top": n_tok,
@@ -603,6 +664,7 @@ def main():
             and args.workload != "specpc_draft_32k":
         print("[bench] timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = speckv_cpu_baseline(cfg, inp)
+
     print(json.dumps(out), flush=True)
 
 
