@@ -117,7 +117,7 @@ def speckv_cpu_baseline(cfg, inp, budget_s=10.0):
                       f"keys: fp64 scores, max-pool, selection, K/V compaction) on a pool of {n} single-threaded "
                       f"worker processes ({len(os.sched_getaffinity(0))} cores in the affinity mask): {wall:.1f} s "
                       f"wall, {busy:.1f} s in the workers",
-            "single_core_extrapolated": {"unit_s": round(t1, 3), "units": len(units), "step_s": round(step_1core, 1),
+            "single_core_extrapolated": {"unit_s": round(t1, 4), "units": len(units), "step_s": round(step_1core, 3),
                                          "value": len(units) * cfg.n_in / step_1core, "unit": "keys/s",
                                          "note": "one unit timed on one core with one BLAS thread, scaled to "
                                                  "every unit of the step"}}
@@ -205,7 +205,7 @@ def specpc_cpu_baseline(cfg, inp):
     return {"value": cfg.n_in / wall, "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"the whole step: {n_maps} causal window maps of {cfg.window} x {cfg.n_keys} over a pool of {n} "
                       f"single-threaded workers, then mean, weighted max, pooling and selection: {wall:.1f} s wall",
-            "single_core_extrapolated": {"map_s": round(t1, 3), "maps": n_maps, "step_s": round(t1 * n_maps, 1),
+            "single_core_extrapolated": {"map_s": round(t1, 4), "maps": n_maps, "step_s": round(t1 * n_maps, 3),
                                          "value": cfg.n_in / (t1 * n_maps), "unit": "tokens/s",
                                          "note": "one map timed on one core, scaled to every map"}}
 

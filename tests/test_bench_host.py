@@ -28,7 +28,7 @@ def test_speckv_baseline_small():
     out = bench.speckv_cpu_baseline(cfg, wl.speckv_inputs(cfg, 3, "cpu"), budget_s=0.2)
     _check_pool_fields(out)
     ex = out["single_core_extrapolated"]
-    assert ex["units"] == 16 and ex["step_s"] == pytest.approx(ex["unit_s"] * 16, rel=1e-2, abs=2e-3)
+    assert ex["units"] == 16 and ex["step_s"] == pytest.approx(ex["unit_s"] * 16, rel=1e-3, abs=2e-3)
 
 
 def test_specpc_baseline_small_and_with_lookahead():
