@@ -353,15 +353,17 @@ skv_status scores_impl(const skv_shape* shape, const void* q_obs, const void* k,
   const SpecKVPlans pp = speckv_plans(d, n_pre);
   const ScoreWs& w = pp.ws;
   if (n_pre == 0) return SKV_OK;
-  if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
   const size_t q_bytes = (size_t)(d.L * d.Hq * n_obs * d.D * d.esize);
   const size_t k_bytes = kv_span(d, rows ? n_src_rows : d.n_in);
   const size_t s_bytes = (size_t)(d.L * d.heads() * n_pre) * sizeof(float);
   if (ranges_overlap(scores, s_bytes, q_obs, q_bytes) || ranges_overlap(scores, s_bytes, k, k_bytes) ||
-      ranges_overlap(scores, s_bytes, ws, w.end) || ranges_overlap(ws, w.end, q_obs, q_bytes) ||
-      ranges_overlap(ws, w.end, k, k_bytes) || (rows && ranges_overlap(rows, (size_t)d.n_in * 4, scores, s_bytes)) ||
-      (rows && ranges_overlap(rows, (size_t)d.n_in * 4, ws, w.end)))
+      (rows && ranges_overlap(rows, (size_t)d.n_in * 4, scores, s_bytes)))
+    return SKV_ERR_ALIAS;
+  // the workspace checks come last
+  if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
+  if (ranges_overlap(scores, s_bytes, ws, w.end) || ranges_overlap(ws, w.end, q_obs, q_bytes) ||
+      ranges_overlap(ws, w.end, k, k_bytes) || (rows && ranges_overlap(rows, (size_t)d.n_in * 4, ws, w.end)))
     return SKV_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ScoreArgs a{};

@@ -117,6 +117,91 @@ __global__ __launch_bounds__(1024) void exp_kernel(int iters, float seed, float*
   clock_mark(clk, 1);
 }
 
+// Independent chains of one VALU operation (fma or add) per thread, eight per
+// step, for the issue rate of plain fp32 vector instructions.
+template <bool FMA>
+__global__ __launch_bounds__(1024) void valu_kernel(int iters, float seed, float* sink, unsigned long long* clk) {
+  clock_mark(clk, 0);
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = seed * (float)(threadIdx.x % 5 + j);
+  const float m = 1.0000001f, a = 1e-7f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = FMA ? __builtin_fmaf(x[j], m, a) : x[j] + a;
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t += x[j];
+  if (t == 1234.5f) sink[0] = t;
+  clock_mark(clk, 1);
+}
+
+// The scoring passes' instruction mix, from registers only (no memory
+// traffic): per step a wave forms KT tiles of 32 x 32 scores, each from NV
+// 32x32x16 bf16 MFMAs (NV = head_dim / 16), and then per lane 16 elements of
+// fma -> exp2 -> add per tile, as both scoring passes do.  MODE 0: the mix;
+// MODE 1: the MFMAs alone (one add per tile keeps them live); MODE 2: the
+// vector work alone (on values the compiler cannot precompute).  PRIO raises
+// the issue priority around the MFMAs, as the scoring kernels do at two waves
+// per SIMD.  The empty asm statements mark the row operand as changed every
+// step, so that nothing is hoisted out of the loop; they emit no instruction.
+template <int KT, int NV, int MODE, bool PRIO, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void mix_kernel(int iters, float seed, float* sink,
+                                                             unsigned long long* clk) {
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  clock_mark(clk, 0);
+  const unsigned lane = threadIdx.x % 64;
+  u32x4 a[KT][NV], b[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    b[v] = u32x4{0x3f803f80u ^ lane, 0x3e003f00u, 0xbf00be80u + v, 0x3c003c00u};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) a[kt][v] = u32x4{0x3f00bf00u + lane, 0x3e80be80u ^ kt, 0x3d003d80u, 0x3f803f00u + v};
+  }
+  const float c = seed, ref = 3.0f;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 vals[KT];  // MODE 2: the "scores", set once and marked as changed every step
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vals[kt][i] = (float)(i + kt) * seed;
+  for (int it = 0; it < iters; ++it) {
+    f32x16 acc[KT];
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        asm volatile("" : "+v"(vals[kt]));
+        acc[kt] = vals[kt];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) asm volatile("" : "+v"(b[v]));
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kt][v]),
+                                                            __builtin_bit_cast(bf16x8, b[v]), acc[kt], 0, 0, 0);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s4[kt & 3] += acc[kt][0];
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[kt][i], c, -ref));
+    }
+  }
+  const float t = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  if (t == 1234.5f) sink[0] = t;
+  clock_mark(clk, 1);
+}
+
 struct Result {
   float ms;
   double ghz;
@@ -199,6 +284,43 @@ int main(int argc, char** argv) {
     exp_r[k] = time_best([&] { exp_kernel<<<cus, threads>>>(exp_iters, 0.1f, fsink, d_clk); }, d_clk);
     exp_t[k] = (double)cus * threads * exp_iters * 8 / (exp_r[k].ms * 1e-3) * 1e-12;
   }
+  // Issue cost of plain fp32 vector instructions (4 waves per SIMD).
+  const int valu_iters = small ? 200 : 400000;
+  const Result fma_r = time_best([&] { valu_kernel<true><<<cus, 1024>>>(valu_iters, 0.1f, fsink, d_clk); }, d_clk);
+  const Result add_r = time_best([&] { valu_kernel<false><<<cus, 1024>>>(valu_iters, 0.1f, fsink, d_clk); }, d_clk);
+  // cycles of one wave64 instruction on a SIMD: time x clock / (instructions per SIMD)
+  auto instr_cycles = [&](const Result& r, double per_simd) { return r.ms * 1e-3 * r.ghz * 1e9 / per_simd; };
+  const double fma_cyc = instr_cycles(fma_r, 4.0 * valu_iters * 8);
+  const double add_cyc = instr_cycles(add_r, 4.0 * valu_iters * 8);
+  const double exp_cyc = instr_cycles(exp_r[1], 4.0 * exp_iters * 8);
+
+  // The scoring instruction mix: cycles per 32 x 32 score tile on one SIMD.
+  struct Mix {
+    const char* name;
+    int kt, waves;
+    Result r;
+    int iters;
+  };
+  const int tiles = small ? 800 : 160000;  // tiles per wave per launch
+  Mix mixes[] = {
+      {"d128_mfma_only_2w", 4, 8, {}, 0},       {"d128_valu_only_2w", 4, 8, {}, 0},
+      {"d128_valu_only_4w", 4, 16, {}, 0},      {"d128_mix_2w", 4, 8, {}, 0},
+      {"d128_mix_2w_prio", 4, 8, {}, 0},        {"d128_mix_3w_kt2", 2, 12, {}, 0},
+      {"d128_mix_3w_kt2_prio", 2, 12, {}, 0},   {"d64_mfma_only_3w", 4, 12, {}, 0},
+      {"d64_mix_3w", 4, 12, {}, 0},             {"d64_mix_2w_prio", 4, 8, {}, 0},
+  };
+  for (Mix& m : mixes) m.iters = tiles / m.kt;
+  const float c = 0.1275f;
+  mixes[0].r = time_best([&] { mix_kernel<4, 8, 1, false, 8><<<cus, 512>>>(mixes[0].iters, c, fsink, d_clk); }, d_clk);
+  mixes[1].r = time_best([&] { mix_kernel<4, 8, 2, false, 8><<<cus, 512>>>(mixes[1].iters, c, fsink, d_clk); }, d_clk);
+  mixes[2].r = time_best([&] { mix_kernel<4, 8, 2, false, 16><<<cus, 1024>>>(mixes[2].iters, c, fsink, d_clk); }, d_clk);
+  mixes[3].r = time_best([&] { mix_kernel<4, 8, 0, false, 8><<<cus, 512>>>(mixes[3].iters, c, fsink, d_clk); }, d_clk);
+  mixes[4].r = time_best([&] { mix_kernel<4, 8, 0, true, 8><<<cus, 512>>>(mixes[4].iters, c, fsink, d_clk); }, d_clk);
+  mixes[5].r = time_best([&] { mix_kernel<2, 8, 0, false, 12><<<cus, 768>>>(mixes[5].iters, c, fsink, d_clk); }, d_clk);
+  mixes[6].r = time_best([&] { mix_kernel<2, 8, 0, true, 12><<<cus, 768>>>(mixes[6].iters, c, fsink, d_clk); }, d_clk);
+  mixes[7].r = time_best([&] { mix_kernel<4, 4, 1, false, 12><<<cus, 768>>>(mixes[7].iters, c, fsink, d_clk); }, d_clk);
+  mixes[8].r = time_best([&] { mix_kernel<4, 4, 0, false, 12><<<cus, 768>>>(mixes[8].iters, c, fsink, d_clk); }, d_clk);
+  mixes[9].r = time_best([&] { mix_kernel<4, 4, 0, true, 8><<<cus, 512>>>(mixes[9].iters, c, fsink, d_clk); }, d_clk);
   CK(hipDeviceSynchronize());
 
   std::printf("device %s, %d CUs, wall clock %d kHz\n", prop.gcnArchName, cus, wall_khz);
@@ -212,11 +334,30 @@ int main(int argc, char** argv) {
   for (int k = 0; k < 2; ++k)
     std::printf("v_exp_f32  %d waves/SIMD %8.3f ms  %7.2f T exp/s                      clock %.2f GHz\n",
                 k == 0 ? 2 : 4, exp_r[k].ms, exp_t[k], exp_r[k].ghz);
+  std::printf("valu (4 waves/SIMD): v_fma_f32 %.2f, v_add_f32 %.2f, v_exp_f32 %.2f cycles per wave64 instruction "
+              "(clocks %.2f / %.2f / %.2f GHz)\n",
+              fma_cyc, add_cyc, exp_cyc, fma_r.ghz, add_r.ghz, exp_r[1].ghz);
+  std::printf("scoring mix, cycles per 32x32 score tile on one SIMD (actual clock; nominal = at 2.4 GHz):\n");
+  for (const Mix& m : mixes) {
+    const int wps = m.waves / 4;
+    const double per_simd = (double)wps * m.iters * m.kt;
+    const double cyc = m.r.ms * 1e-3 * m.r.ghz * 1e9 / per_simd;
+    const double nom = m.r.ms * 1e-3 * 2.4e9 / per_simd;
+    std::printf("  %-22s %8.3f ms  %7.1f cycles  %7.1f nominal  clock %.2f GHz\n", m.name, m.r.ms, cyc, nom, m.r.ghz);
+  }
   std::printf("{\"hbm_read_GBps\": %.1f, \"hbm_copy_GBps\": %.1f, \"mfma_bf16_TFLOPs\": [%.1f, %.1f], "
               "\"exp_T_per_s\": [%.3f, %.3f], \"clock_GHz\": {\"read\": %.3f, \"copy\": %.3f, \"mfma\": [%.3f, %.3f], "
-              "\"exp\": [%.3f, %.3f]}, \"small\": %s}\n",
+              "\"exp\": [%.3f, %.3f]}, \"valu_cycles\": {\"fma\": %.3f, \"add\": %.3f, \"exp\": %.3f}, \"mix\": {",
               rd_gbs, cp_gbs, mfma_tf[0], mfma_tf[1], exp_t[0], exp_t[1], rd.ghz, cp.ghz, mfma_r[0].ghz,
-              mfma_r[1].ghz, exp_r[0].ghz, exp_r[1].ghz, small ? "true" : "false");
+              mfma_r[1].ghz, exp_r[0].ghz, exp_r[1].ghz, fma_cyc, add_cyc, exp_cyc);
+  for (size_t i = 0; i < sizeof(mixes) / sizeof(mixes[0]); ++i) {
+    const Mix& m = mixes[i];
+    const double per_simd = (double)(m.waves / 4) * m.iters * m.kt;
+    std::printf("%s\"%s\": {\"cycles_per_tile\": %.2f, \"nominal_cycles_per_tile\": %.2f, \"clock_GHz\": %.3f}",
+                i ? ", " : "", m.name, m.r.ms * 1e-3 * m.r.ghz * 1e9 / per_simd, m.r.ms * 1e-3 * 2.4e9 / per_simd,
+                m.r.ghz);
+  }
+  std::printf("}, \"small\": %s}\n", small ? "true" : "false");
   CK(hipFree(src));
   CK(hipFree(dst));
   CK(hipFree(usink));

@@ -310,8 +310,7 @@ def bench_speckv(args, cfg, torch, skv, wl):
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
     # digests of the inputs as generated (the in-place workload overwrites its K/V during the steps)
-    combined, per_layer = input_digests({"q_obs": inp["q_obs"], "k": inp["k"], "v": inp["v"]})
-    print("[bench] input sha256 per layer: " + json.dumps(per_layer), file=sys.stderr, flush=True)
+    combined, _ = input_digests({"q_obs": inp["q_obs"], "k": inp["k"], "v": inp["v"]})
     digests = {"scheme": "sha256 of the raw bytes of each (layer, tensor); per tensor, sha256 of its layer digests "
                          "(hex, in layer order) concatenated", **combined}
     L, Hkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim

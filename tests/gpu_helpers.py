@@ -98,3 +98,53 @@ def assert_compacted(k_c, v_c, k, v, kept):
 
 def np64(t):
     return wl.to_numpy_f64(t)
+
+
+def raw_host(t):
+    """Host copy of a tensor's raw elements (bfloat16 as uint16 words, float32 as is), for the oracle pool."""
+    t = t.detach().contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def check_every_unit_against_oracle(scores, pooled, kept, q_obs, k, cfg, per_query_head=False, aggregation="sum",
+                                    layer_ids=None, label=""):
+    """Compares EVERY (layer, head) unit of a GPU launch with the fp64 oracle,
+    the oracle spread over a pool of single-threaded worker processes.
+
+    scores, pooled, kept: host arrays [L, H, ...] from the GPU; q_obs, k:
+    the inputs (device or host tensors) [L, Hq, n_obs, d] and [L, Hkv, n_in, d].
+    Per unit: scores within the tolerance, the selection rule exact on the
+    GPU's own pooled scores and equal to the oracle's up to ties within the
+    tolerance.  layer_ids names the layers in messages (default 0 ..)."""
+    import time
+    import oracle
+    from oracle.pool import OraclePool, worker_count
+    L, H = kept.shape[:2]
+    G = cfg.G
+    rows = 1 if per_query_head else G
+    layer_ids = list(range(L)) if layer_ids is None else list(layer_ids)
+    q_raw, k_raw = raw_host(q_obs), raw_host(k)
+    scale = oracle.default_scale(cfg.head_dim)
+
+    def tasks():
+        for u in range(L * H):
+            layer, h = divmod(u, H)
+            q = q_raw[layer, h:h + 1] if per_query_head else q_raw[layer, h * G:(h + 1) * G]
+            kvh = h // G if per_query_head else h
+            yield dict(uid=u, q=q, k=k_raw[layer, kvh], n_pre=cfg.n_pre, scale=scale, aggregation=aggregation)
+
+    n = worker_count()
+    print(f"[oracle] {label}: {L * H} units on {n} worker processes", flush=True)
+    t0, done = time.perf_counter(), 0
+    with OraclePool(n) as pool:
+        for u, want, _ in pool.imap("speckv", tasks()):
+            layer, h = divmod(u, H)
+            where = f"{label}[layer {layer_ids[layer]}, head {h}]"
+            assert_scores_close(scores[layer, h], want, rows, cfg.n_obs, f"scores{where}")
+            assert_kept_matches(kept[layer, h][None], pooled[layer, h][None],
+                                oracle.pool1d(want, cfg.pool_kernel, "max")[None], cfg.C_max, cfg.n_window,
+                                f"kept{where}")
+            done += 1
+            if done % 64 == 0 or done == L * H:
+                print(f"[oracle] {label}: {done} of {L * H} units match ({time.perf_counter() - t0:.0f} s)",
+                      flush=True)

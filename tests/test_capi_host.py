@@ -106,8 +106,9 @@ def test_scores_rejects_bad_pointers_and_workspace(lib):
     _, nbytes = _ws_bytes(lib, s)
     assert lib.speckv_scores(ctypes.byref(s), P(257), P(512), P(1024), P(4096), nbytes, None) == ALIGN
     assert lib.speckv_scores(ctypes.byref(s), P(256), P(520), P(1024), P(4096), nbytes, None) == ALIGN
-    assert lib.speckv_scores(ctypes.byref(s), P(256), P(512), P(1024), None, nbytes, None) == WS
-    assert lib.speckv_scores(ctypes.byref(s), P(256), P(512), P(1024), P(4096), 100, None) == WS
+    q, k, sc = P(1 << 30), P(2 << 30), P(3 << 30)  # disjoint spans (overlaps are checked before the workspace)
+    assert lib.speckv_scores(ctypes.byref(s), q, k, sc, None, nbytes, None) == WS
+    assert lib.speckv_scores(ctypes.byref(s), q, k, sc, P(4 << 30), 100, None) == WS
     s0 = shape(n_window=0, n_lookahead=0)
     assert lib.speckv_scores(ctypes.byref(s0), P(256), P(512), P(1024), P(4096), nbytes, None) == SHAPE
     # nothing to score: accepted without touching the device
@@ -336,3 +337,4 @@ def test_in_place_compact_rejects_kept_inside_staging(lib):
 
 def test_internal_status_is_named(lib):
     assert lib.speckv_status_string(9) == b"host-side failure inside the library"
+
