@@ -16,6 +16,7 @@ from ._lib import SKV_AGG_MAX, SKV_AGG_SUM, SKV_BF16, SKV_F32, SKV_POOL_AVG, SKV
 
 __all__ = [
     "Shape", "SpecKVError", "make_shape", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores",
+    "speckv_scores_noalloc",
     "speckv_select", "speckv_compact", "specpc_gather_tokens", "specpc_token_scores",
     "speckv_decode_workspace_bytes", "speckv_decode_attention", "profile_enable", "profile_read",
     "SKV_F32", "SKV_BF16", "SKV_POOL_NONE", "SKV_POOL_MAX", "SKV_POOL_AVG", "SKV_AGG_SUM", "SKV_AGG_MAX",
@@ -76,6 +77,12 @@ def speckv_scores(shape: Shape, q_obs, k, scores, workspace, stream=None):
     w, wb = _ws(workspace)
     _check(_lib.load().speckv_scores(ctypes.byref(shape), _ptr(q_obs, "q_obs"), _ptr(k, "k"), _ptr(scores, "scores"),
                                      w, wb, _stream(stream)), "speckv_scores")
+
+
+def speckv_scores_noalloc(shape: Shape, q_obs, k, scores, stream=None):
+    """speckv_scores with the library's fixed per-GPU scratch instead of a workspace."""
+    _check(_lib.load().speckv_scores_noalloc(ctypes.byref(shape), _ptr(q_obs, "q_obs"), _ptr(k, "k"),
+                                             _ptr(scores, "scores"), _stream(stream)), "speckv_scores_noalloc")
 
 
 def speckv_select(shape: Shape, scores, C_max: int, pool: int, pool_kernel: int, kept, pooled, workspace,

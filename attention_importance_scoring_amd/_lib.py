@@ -25,7 +25,7 @@ EXPORTED = (
     "speckv_status_string", "speckv_workspace_bytes", "speckv_n_keep", "speckv_scores", "speckv_select",
     "speckv_compact", "specpc_gather_tokens", "speckv_scores_rows", "speckv_compact_rows", "specpc_token_scores",
     "speckv_decode_workspace_bytes", "speckv_decode_attention", "speckv_profile_enable", "speckv_profile_count",
-    "speckv_profile_read",
+    "speckv_profile_read", "speckv_scores_noalloc",
 )
 
 
@@ -59,6 +59,8 @@ def load(path: str | None = None):
     lib.speckv_n_keep.argtypes = [S, c_int32, ctypes.POINTER(c_int64)]
     lib.speckv_scores.restype = c_int32
     lib.speckv_scores.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.speckv_scores_noalloc.restype = c_int32
+    lib.speckv_scores_noalloc.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.speckv_select.restype = c_int32
     lib.speckv_select.argtypes = [S, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]

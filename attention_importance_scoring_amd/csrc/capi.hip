@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 using namespace skv;
@@ -359,7 +360,7 @@ skv_status scores_impl(const skv_shape* shape, const void* q_obs, const void* k,
   if (ranges_overlap(scores, s_bytes, q_obs, q_bytes) || ranges_overlap(scores, s_bytes, k, k_bytes) ||
       (rows && ranges_overlap(rows, (size_t)d.n_in * 4, scores, s_bytes)))
     return SKV_ERR_ALIAS;
-  // the workspace checks come last
+  // the workspace checks come last (the allocation-free variant relies on it)
   if (!ws || ws_bytes < w.end) return SKV_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKV_ERR_ALIGN;
   if (ranges_overlap(scores, s_bytes, ws, w.end) || ranges_overlap(ws, w.end, q_obs, q_bytes) ||
@@ -419,6 +420,67 @@ skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* 
                          size_t ws_bytes, void* stream) {
   return guard([&]() -> skv_status {
     return scores_impl(shape, q_obs, k, nullptr, 0, scores, ws, ws_bytes, stream);
+  });
+}
+
+}  // extern "C"
+
+// Scratch of speckv_scores_noalloc: a fixed device array instead of a
+// caller workspace, one copy per GPU (each GPU that runs the library holds
+// it until the process ends).  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is looked up once
+// per GPU and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device (looked up on
+// the first call there, with that device current).
+skv_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SKV_ERR_HIP;
+  if (dev >= kMaxDevices) return SKV_ERR_PARAM;
+  if (stream) {  // the scratch belongs to the current device: the stream must too
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SKV_ERR_HIP;
+    if (sdev != dev) return SKV_ERR_PARAM;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status speckv_scores_noalloc(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
+                                 void* stream) {
+  return guard([&]() -> skv_status {
+    // Argument checks first (no HIP call on an invalid argument): the
+    // scratch then stands in for the workspace, with the same layout.  The
+    // pass-1 partials, the row normalisers and the extra column sums are all
+    // written before they are read, so the previous call's contents need no
+    // clearing.
+    const skv_status pre = scores_impl(shape, q_obs, k, nullptr, 0, scores, nullptr, 0, nullptr);
+    if (pre != SKV_ERR_WORKSPACE) return pre;  // an argument error, or nothing to score (SKV_OK)
+    Dims d;
+    SKV_TRY(check_shape(shape, &d));
+    if (speckv_plans(d, d.n_in - d.n_window).ws.end > kNoAllocScratchBytes)
+      return SKV_ERR_WORKSPACE;  // needs more than the fixed scratch
+    void* ws = nullptr;
+    SKV_TRY(scratch_address(static_cast<hipStream_t>(stream), &ws));
+    return scores_impl(shape, q_obs, k, nullptr, 0, scores, ws, kNoAllocScratchBytes, stream);
   });
 }
 

@@ -129,6 +129,23 @@ skv_status speckv_n_keep(const skv_shape* shape, int32_t C_max, int64_t* out_n_k
 skv_status speckv_scores(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* speckv_scores without a workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as speckv_scores
+ * (bit-identical scores), with a fixed scratch array of 64 MiB inside the
+ * library standing in for the workspace: one copy per GPU, held from the
+ * first call on that GPU until the process ends.  The call allocates and
+ * frees nothing.  It returns SKV_ERR_WORKSPACE when the problem needs more
+ * scratch than that (e.g. up to 30 of the 64 layers of the 64K
+ * Qwen2.5-32B-shaped workload fit per call, and up to 7 layers of the 128K
+ * Llama-3.1-8B-shaped one), and
+ * SKV_ERR_PARAM when `stream` belongs to a device other than the current one.
+ * Every call on one GPU uses the same scratch: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Nothing in the scratch needs clearing between calls. */
+skv_status speckv_scores_noalloc(const skv_shape* shape, const void* q_obs, const void* k, float* scores,
+                                 void* stream);
+
 /* SpecKV selection ("Key designs", SpecKV; "Loss / training strategy",
  * local pooling).  Per head: pooled = pool1d(scores) over the n_pre prefix
  * scores (stride 1, odd pool_kernel in 1 .. 4097, windows truncated at both

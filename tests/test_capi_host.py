@@ -338,3 +338,28 @@ def test_in_place_compact_rejects_kept_inside_staging(lib):
 def test_internal_status_is_named(lib):
     assert lib.speckv_status_string(9) == b"host-side failure inside the library"
 
+
+def test_noalloc_scores_rejections_on_the_host(lib):
+    # Argument errors come first (no HIP call); a problem larger than the fixed
+    # 64 MiB scratch is refused before anything touches the device.
+    f = lambda s, q, k, sc: lib.speckv_scores_noalloc(ctypes.byref(s), P(q), P(k), P(sc), None)
+    s = shape()
+    assert f(s, 0, 2 << 30, 3 << 30) == NULL
+    assert f(s, (1 << 30) + 2, 2 << 30, 3 << 30) == ALIGN
+    assert f(s, 1 << 30, 2 << 30, (1 << 30) + 4096) == ALIAS
+    assert lib.speckv_scores_noalloc(None, P(1 << 30), P(2 << 30), P(3 << 30), None) == NULL
+    assert f(shape(n_window=1000), 1 << 30, 2 << 30, 3 << 30) == OK  # nothing to score
+    qwen64 = skv.make_shape(64, 40, 8, 128, 65536, 32, 128, skv.SKV_BF16)
+    assert f(qwen64, 1 << 30, 1 << 36, 1 << 40) == WS  # about 142 MB of scratch needed (K spans 8.6 GB)
+
+
+def test_noalloc_scratch_limit_on_the_host(lib):
+    # 30 layers of the 64K Qwen-shaped workload fit the 64 MiB scratch, 31 do not: a fitting shape passes
+    # every check and stops at the first HIP call here (no GPU), one that does not is refused before it
+    f = lambda L: lib.speckv_scores_noalloc(ctypes.byref(skv.make_shape(L, 40, 8, 128, 65536, 32, 128,
+                                                                         skv.SKV_BF16)),
+                                            P(1 << 30), P(1 << 36), P(1 << 42), None)
+    assert f(31) == WS
+    import torch
+    if torch.cuda.device_count() == 0:  # on a GPU machine a fitting shape would launch on the fake pointers
+        assert f(30) == 8  # SKV_ERR_HIP: no device
