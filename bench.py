@@ -25,9 +25,19 @@ METRIC = "keys scored+compacted/sec and % of HBM/MFMA roofline at n_in=64K, 32B 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-# v_exp_f32: 256 CUs x 32 exponentials per clock (one wave64 instruction per 8 cycles on each of the 4 SIMDs)
-# x 2.4 GHz; the peak-check program measures 17.4 T/s, about 9 cycles per instruction.
-PEAK_EXP_TPS = 256 * 32 * 2.4e9 / 1e12
+# Vector-unit ceiling of the scoring work, from the chip's unit counts (256 CUs x 4 SIMDs x 64 lanes, 2.4 GHz)
+# and the issue cost of each wave64 instruction measured by the peak-check program
+# (profiles/unit_peaks_hbm_mfma_valu_mix.txt; no published figure exists for gfx950's transcendental rate):
+# v_fma_f32 3.05, v_exp_f32 9.04, v_add_f32 4.49 cycles.  Every scored element costs one of each (scale and
+# shift, exponential, accumulation), so a SIMD retires 64 elements per 16.58 cycles.
+ISSUE_CYCLES = {"fma": 3.05, "exp": 9.04, "add": 4.49}
+PEAK_EXP_TPS = 256 * 4 * 64 / ISSUE_CYCLES["exp"] * 2.4e9 / 1e12               # 17.4 T exp/s
+PEAK_ELEM_TPS = 256 * 4 * 64 / sum(ISSUE_CYCLES.values()) * 2.4e9 / 1e12       # 9.49 T elements/s
+# The two together at head_dim 128: 8 MFMAs and 16 elements per lane per 32 x 32 score tile take 412 cycles on
+# a SIMD at two waves per SIMD with the MFMA issue priority (the scoring kernels' form; the MFMAs alone take
+# 269, the vector work alone 259): at 2.4 GHz, 256 x 4 x 1024 / 412 x 2.4e9 elements/s.
+MIX_CYCLES_PER_TILE_D128 = 412.1
+PEAK_MIX_ELEM_TPS = 256 * 4 * 1024 / MIX_CYCLES_PER_TILE_D128 * 2.4e9 / 1e12  # 6.11 T elements/s
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -374,6 +384,19 @@ def bench_speckv(args, cfg, torch, skv, wl):
             "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name, f"speckv_kernels_{cfg.name}_traffic.json") if default_variant else None}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
     path_frac = (flops_per_pass / (ms * 1e-3) / 1e12) / peak
+    # per pass: one Q_obs K^T on MFMA and one scale-exp-add per score element on the vector units
+    elems_per_pass = flops_per_pass / (2.0 * d)
+    passes = {}
+    for k in ("score_pass1", "score_pass2"):
+        t = kern[k]["ms_per_step"] * 1e-3
+        passes[k] = {"ms": round(kern[k]["ms_per_step"], 4),
+                     "mfma_frac": round(flops_per_pass / t / 1e12 / peak, 4),
+                     "alu_frac": round(elems_per_pass / t / 1e12 / PEAK_ELEM_TPS, 4)}
+        if d == 128 and cfg.dtype == "bf16":
+            passes[k]["mix_frac"] = round(elems_per_pass / t / 1e12 / PEAK_MIX_ELEM_TPS, 4)
+    roof_alu = {"kernel": dom, "bound": "alu", "achieved": round(elems_per_pass / launches_per_step / avg_s / 1e12, 3),
+                "peak": round(PEAK_ELEM_TPS, 3), "unit": "T elements/s (fma + exp2 + add each)",
+                "frac": round(elems_per_pass / launches_per_step / avg_s / 1e12 / PEAK_ELEM_TPS, 4)}
     path = {"scope": "the whole step (scores + select + compact), one Q_obs K^T of algorithmic flops",
             "frac": round(path_frac, 4), "target_frac": 0.40,
             "ms_at_target": round(flops_per_pass / (0.40 * peak * 1e12) * 1e3, 3), "ms_measured": round(ms, 4)}
@@ -386,6 +409,8 @@ def bench_speckv(args, cfg, torch, skv, wl):
                    "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys,
                    "aggregation": args.aggregation, "per_query_head": bool(args.per_query_head)},
         "roofline": roof,
+        "roofline_alu": roof_alu,
+        "passes": passes,
         "path_mfma_frac": round(path_frac, 4),
         "path_mfma": path,
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "ms_per_step": round(v["ms_per_step"], 4)}
@@ -430,8 +455,9 @@ def bench_specpc(args, cfg, torch, skv, wl):
     dom = max(("score_pass1", "specpc_pass2"), key=lambda k: kern.get(k, {}).get("avg_ms", 0.0))
     achieved = elems / (kern[dom]["avg_ms"] * 1e-3) / 1e12
     default_cfg = args.n_lookahead is None
-    roof = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_EXP_TPS, 2),
-            "unit": "T exp/s", "frac": round(achieved / PEAK_EXP_TPS, 4),
+    roof = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_ELEM_TPS, 3),
+            "unit": "T elements/s (fma + exp2 + add each)", "frac": round(achieved / PEAK_ELEM_TPS, 4),
+            "exp_frac": round(achieved / PEAK_EXP_TPS, 4),
             "traffic": traffic_for(dom, cfg.name, f"specpc_kernels_{cfg.name}_traffic.json") if default_cfg else None}
     return {
         "metric": "SpecPC tokens scored+selected/sec (draft attention stack)", "value": cfg.n_in / (ms * 1e-3),
@@ -442,6 +468,8 @@ def bench_specpc(args, cfg, torch, skv, wl):
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "n_in": cfg.n_in, "window": cfg.window,
                    "n_lookahead": cfg.n_lookahead, "k_top": cfg.k_top},
         "roofline": roof, "exp_rate_per_s": exps_per_s, "kernels": kern,
+        "passes": {k: {"ms": kern[k]["avg_ms"], "alu_frac": round(elems / (kern[k]["avg_ms"] * 1e-3) / 1e12 / PEAK_ELEM_TPS, 4)}
+                   for k in ("score_pass1", "specpc_pass2") if k in kern},
     }, inp
 
 
@@ -512,8 +540,9 @@ def bench_cascade(args, cc, torch, skv, wl):
     pc_maps = (dr.n_layers - dr.l_skip) * dr.n_q_heads
     pc_elems = pc_maps * sum(min(dr.n_keys, dr.n_keys - dr.window + i + 1) for i in range(dr.window))
     pc_ach = pc_elems / (kern["specpc_pass2"]["avg_ms"] * 1e-3) / 1e12
-    roof = {"kernel": "specpc_pass2", "bound": "alu", "achieved": round(pc_ach, 3), "peak": round(PEAK_EXP_TPS, 2),
-            "unit": "T exp/s", "frac": round(pc_ach / PEAK_EXP_TPS, 4),
+    roof = {"kernel": "specpc_pass2", "bound": "alu", "achieved": round(pc_ach, 3), "peak": round(PEAK_ELEM_TPS, 3),
+            "unit": "T elements/s (fma + exp2 + add each)", "frac": round(pc_ach / PEAK_ELEM_TPS, 4),
+            "exp_frac": round(pc_ach / PEAK_EXP_TPS, 4),
             "traffic": traffic_for("specpc_pass2", cc.name, f"cascade_kernels_{cc.name}_traffic.json")}
     # the gather moves n_tok rows of K and V per (layer, KV head) in and out
     g = kern.get("gather_tokens")

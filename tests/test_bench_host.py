@@ -2,7 +2,7 @@
 the SpecKV, SpecPC, cascade and decode lines run on a pool of single-threaded
 workers (one per core, at most 16) and report positive rates with the worker
 count as `cores` and a single-core extrapolation; the step statistics and the
-input digests."""
+input digests; the vector-unit peaks."""
 import dataclasses
 import hashlib
 
@@ -14,8 +14,11 @@ from attention_importance_scoring_amd import workloads as wl
 from oracle.pool import worker_count
 
 
-def test_exp_peak_from_unit_counts():
-    assert bench.PEAK_EXP_TPS == pytest.approx(19.6608)
+def test_vector_peaks_from_unit_counts_and_measured_issue_cycles():
+    # 256 CUs x 4 SIMDs x 64 lanes at 2.4 GHz over the measured wave64 issue cycles
+    assert bench.PEAK_EXP_TPS == pytest.approx(256 * 4 * 64 / 9.04 * 2.4e9 / 1e12)
+    assert bench.PEAK_ELEM_TPS == pytest.approx(256 * 4 * 64 / (3.05 + 9.04 + 4.49) * 2.4e9 / 1e12)
+    assert 9.4 < bench.PEAK_ELEM_TPS < 9.6 and bench.PEAK_MIX_ELEM_TPS < bench.PEAK_ELEM_TPS
 
 
 def _check_pool_fields(out):
