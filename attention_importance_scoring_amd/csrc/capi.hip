@@ -536,9 +536,8 @@ skv_status speckv_compact_rows(const skv_shape* shape, const void* k, const void
     ProfScope p("compact_gather", s);
     g.src = k;
     g.dst = k_out;
-    SKV_TRY(hip_status(launch_gather(g, s)));
-    g.src = v;
-    g.dst = v_out;
+    g.src2 = v;
+    g.dst2 = v_out;
     return hip_status(launch_gather(g, s));
   });
 }
@@ -637,9 +636,8 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
       g.dst_unit_stride = n_keep * row_bytes;
       g.src = k;
       g.dst = k_out;
-      SKV_TRY(hip_status(launch_gather(g, s)));
-      g.src = v;
-      g.dst = v_out;
+      g.src2 = v;
+      g.dst2 = v_out;
       return hip_status(launch_gather(g, s));
     }
     // In place: gather K and V into the workspace, then copy back to rows [0, n_keep).
@@ -661,9 +659,8 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
       g.dst_unit_stride = n_keep * row_bytes;
       g.src = k;
       g.dst = ks;
-      SKV_TRY(hip_status(launch_gather(g, s)));
-      g.src = v;
-      g.dst = vs;
+      g.src2 = v;
+      g.dst2 = vs;
       SKV_TRY(hip_status(launch_gather(g, s)));
     }
     ProfScope p("compact_copyback", s);
@@ -679,9 +676,8 @@ skv_status speckv_compact(const skv_shape* shape, const void* k, const void* v, 
     b.dst_unit_stride = d.stride * d.esize;
     b.src = ks;
     b.dst = const_cast<void*>(k);
-    SKV_TRY(hip_status(launch_gather(b, s)));
-    b.src = vs;
-    b.dst = const_cast<void*>(v);
+    b.src2 = vs;
+    b.dst2 = const_cast<void*>(v);
     return hip_status(launch_gather(b, s));
   });
 }
@@ -719,9 +715,8 @@ skv_status specpc_gather_tokens(const skv_shape* shape, const void* k, const voi
     ProfScope p("gather_tokens", s);
     g.src = k;
     g.dst = k_out;
-    SKV_TRY(hip_status(launch_gather(g, s)));
-    g.src = v;
-    g.dst = v_out;
+    g.src2 = v;
+    g.dst2 = v_out;
     return hip_status(launch_gather(g, s));
   });
 }

@@ -93,10 +93,13 @@ int select_segments(int64_t n_units, int64_t n_pre, int64_t n_top);
 size_t select_candidate_bytes(int64_t n_units, int64_t n_pre, int64_t n_top);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
-// Row gather: dst[u][t] = src[u][idx[u * idx_unit_stride + t]] (or src[u][t] when idx is null).
+// Row gather: dst[u][t] = src[u][idx[u * idx_unit_stride + t]] (or src[u][t] when idx is null);
+// with src2 set, the same gather from src2 into dst2 in the same launch (K and V together).
 struct GatherArgs {
   const void* src;
   void* dst;
+  const void* src2;         // NULL, or a second tensor gathered with the same indices
+  void* dst2;
   const int32_t* idx;       // per-unit lists (idx_unit_stride = n_rows), one shared list (0), or nullptr
   const int32_t* idx2;      // NULL, or a shared list the first index goes through: row idx2[idx[...]]
   int32_t n_idx2;           // entries of idx2 (a first index outside [0, n_idx2) gives a zero row)

@@ -60,8 +60,11 @@ struct ScoreGeom {
   static_assert(KT * 4 * kNV <= 128, "resident keys must fit in 128 VGPRs");
   // Waves per block (one block per CU, kWaves / 4 per SIMD).  At head_dim 64
   // the vector work outweighs the MFMAs, and with at most 64 VGPRs of
-  // resident keys three waves per SIMD fit and raise the issue rate.
+  // resident keys three waves per SIMD fit and raise the issue rate.  (Three
+  // waves with two key tiles at head_dim 128 measured 8-10 % slower on the
+  // 128K in-place workload, whose layers arrive cold, and 10 % slower at 64K.)
   static constexpr int kWaves = (D == 64 && KT * 4 * kNV <= 64) ? 12 : 8;
+  static constexpr bool kPrio = kWaves == 8;  // the MFMA issue priority (nothing gained at 64)
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 32 * kKT;
   static constexpr int kKeysPerSub = kWaves * kKeysPerWave;  // keys resident in one block at a time
@@ -304,7 +307,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         masked = sub_masked(cu.sc);
       }
       u32x4 qf[Gm::kNV];
-      if constexpr (Gm::kWaves == 8) mfma_prio<1>();
+      if constexpr (Gm::kPrio) mfma_prio<1>();
       read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
       f32x16 acc[Gm::kKT];
       const int r = cu.rt * 32 + lane % 32;
@@ -312,7 +315,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         pass1_mfma<T, D, KT, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
       else
         pass1_mfma<T, D, KT, false>(kst, qf, 0, acc);
-      if constexpr (Gm::kWaves == 8) mfma_prio<0>();
+      if constexpr (Gm::kPrio) mfma_prio<0>();
       RowStat st;
       if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
         st = masked ? pass1_stats<T, D, KT, true>(acc, c) : pass1_stats<T, D, KT, false>(acc, c);
@@ -475,10 +478,10 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
       read_lam(cu.rt, lam);
       f32x16 acc[Gm::kKT];
       u32x4 qf[Gm::kNV];
-      if constexpr (Gm::kWaves == 8) mfma_prio<1>();
+      if constexpr (Gm::kPrio) mfma_prio<1>();
       read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
       pass2_mfma<T, D, KT>(kst, qf, acc);
-      if constexpr (Gm::kWaves == 8) mfma_prio<0>();
+      if constexpr (Gm::kPrio) mfma_prio<0>();
       // acc[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
 #pragma unroll
       for (int kt = 0; kt < Gm::kKT; ++kt) {

@@ -564,17 +564,19 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   if (a.idx2) src_row = (src_row >= 0 && src_row < a.n_idx2) ? a.idx2[src_row] : -1;
   // source unit: same layer, head (unit % units_per_layer) / src_repeat
   const int64_t src_unit = (unit / a.units_per_layer) * a.src_units_per_layer + (unit % a.units_per_layer) / a.src_repeat;
-  char* dst = static_cast<char*>(a.dst) + unit * a.dst_unit_stride + (int64_t)row * a.row_bytes + col * 16;
+  const char* src = static_cast<const char*>(blockIdx.y ? a.src2 : a.src);  // grid row 1: the second tensor
+  char* dst = static_cast<char*>(blockIdx.y ? a.dst2 : a.dst) + unit * a.dst_unit_stride + (int64_t)row * a.row_bytes +
+              col * 16;
   u32x4 v = {0u, 0u, 0u, 0u};
   if (src_row >= 0 && src_row < a.n_src_rows)
-    v = ldg16(static_cast<const char*>(a.src) + src_unit * a.src_unit_stride + (int64_t)src_row * a.row_bytes + col * 16);
+    v = ldg16(src + src_unit * a.src_unit_stride + (int64_t)src_row * a.row_bytes + col * 16);
   *reinterpret_cast<u32x4*>(dst) = v;
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   const int64_t per_unit = (int64_t)a.n_rows * (a.row_bytes / 16);
   const int64_t blocks = (per_unit + 255) / 256 * a.n_units;
-  gather_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  gather_kernel<<<dim3((unsigned)blocks, a.src2 ? 2u : 1u), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
