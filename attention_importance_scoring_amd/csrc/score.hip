@@ -255,13 +255,6 @@ __device__ __forceinline__ float pass1_sum_ref(const f32x16 (&acc)[ScoreGeom<T, 
   return s + shfl_xor32(s);
 }
 
-// Moves the power-of-two part of the sum into the reference: s in [0.5, 1).
-__device__ __forceinline__ RowStat renormalize(RowStat st) {
-  int e;
-  const float mant = frexpf(st.s, &e);
-  return {st.m + (float)e, mant};
-}
-
 template <typename T, int D, int KT, bool ROWS>
 __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass1_kernel(ScoreArgs a) {
   using Gm = ScoreGeom<T, D, KT>;
@@ -320,10 +313,11 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
       if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
         st = masked ? pass1_stats<T, D, KT, true>(acc, c) : pass1_stats<T, D, KT, false>(acc, c);
       } else {
-        // Later visits sum against the row's running reference, which after
-        // renormalization is within one of log2 of the sum so far: no per-tile
-        // max and no rescaling.  A wave falls back to the exact merge when a
-        // row has no reference yet or a tile would exceed it by 2^64.
+        // Later visits sum against the row's reference (the maximum of its
+        // first visit, raised only by an exact merge): no per-tile max and no
+        // rescaling.  A wave falls back to the exact merge when a row has no
+        // reference yet or a tile would exceed it by 2^64; the running sum
+        // then stays below 2^64 times the keys visited, far inside fp32.
         const RowStat cur = ws[r];  // lanes l and l ^ 32 read the same row
         const float add = pass1_sum_ref<T, D, KT>(acc, c, cur.m);
         if (__any(!(add <= 0x1p64f)))
@@ -331,7 +325,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         else
           st = {cur.m, cur.s + add};
       }
-      if (lane < 32) ws[r] = renormalize(st);  // this wave's own slice: no other wave touches it
+      if (lane < 32) ws[r] = st;  // this wave's own slice: no other wave touches it
     }
     __syncthreads();
     for (int r = threadIdx.x; r < prow; r += Gm::kThreads) {
