@@ -505,9 +505,10 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
 
 template <typename T, int D, int KT>
 static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl,
-                     int64_t target_blocks = SKV_TARGET_BLOCKS) {
+                     int64_t target_blocks = SKV_TARGET_BLOCKS, int64_t extra_parts = 0) {
   using Gm = ScoreGeom<T, D, KT>;
-  // Row parts: as many 32-row tiles as the LDS budget holds, split evenly.
+  // Row parts: as many 32-row tiles as the LDS budget holds (or extra_parts
+  // more parts than that needs), split evenly.
   const int64_t tiles = (n_rows + 31) / 32;
   const int64_t per_row1 = Gm::kRowPitch + (int64_t)Gm::kWaves * (int64_t)sizeof(RowStat);
   const int64_t per_row2 = Gm::kRowPitch + 4;
@@ -515,7 +516,8 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
   const int64_t fit2 = kScoreLdsBudget / (32 * per_row2);
   fit = fit < fit2 ? fit : fit2;
   if (fit < 1) fit = 1;
-  const int64_t parts = (tiles + fit - 1) / fit;
+  int64_t parts = (tiles + fit - 1) / fit + extra_parts;
+  parts = parts > tiles ? tiles : parts;
   const int64_t tpp = (tiles + parts - 1) / parts;
   pl->rows_per_part = (int32_t)(tpp * 32);
   pl->n_parts = (int32_t)((tiles + tpp - 1) / tpp);
@@ -538,8 +540,10 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
 // Four key tiles per wave halve the LDS reads of the row operand per MFMA,
 // but coarsen the key split: they are taken only where the resident-key
 // registers allow them and every block still walks many key groups.  When
-// that needs fewer, longer blocks than the usual target, four tiles still
-// win as long as every CU gets a block (one round of blocks, no tail).
+// that needs fewer, longer blocks than the usual target (few units with long
+// keys), four tiles still win where the blocks make whole rounds over the
+// CUs (no tail): the row parts may then be cut one or two finer than the LDS
+// budget needs, and the plan with the fewest rounds is taken.
 template <typename T, int D>
 static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   plan_for<T, D, 2>(n_units, n_rows, n_keys, pl);
@@ -551,8 +555,19 @@ static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan
       *pl = p4;
       return;
     }
-    plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4, kCUs);
-    if (p4.n_sub >= 16 && n_units * p4.n_parts * p4.n_chunks >= kCUs) *pl = p4;
+    int64_t best_rounds = 0;
+    for (int64_t extra = 0; extra <= 2; ++extra) {
+      for (int64_t rounds = 1; rounds <= 4; ++rounds) {
+        plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4, rounds * kCUs, extra);
+        const int64_t blocks = n_units * p4.n_parts * p4.n_chunks;
+        if (p4.n_sub < 16 || blocks % kCUs != 0) continue;
+        if (best_rounds == 0 || blocks / kCUs < best_rounds) {
+          best_rounds = blocks / kCUs;
+          *pl = p4;
+        }
+        break;
+      }
+    }
   }
 }
 

@@ -65,6 +65,9 @@ def parse():
                    help="also run a plain device copy of this many MiB (counter calibration runs)")
     p.add_argument("--cascade-path", choices=["rows", "gather"], default="rows",
                    help="cascade: SpecKV through the kept-token list, or on a gathered copy of the target cache")
+    p.add_argument("--serial-layers", action="store_true",
+                   help="in-place workload: run each layer's selection and compaction on the scoring stream, "
+                        "after its scores (default: on a second stream, beside the next layer's scoring)")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -342,6 +345,15 @@ def bench_speckv(args, cfg, torch, skv, wl):
     vc = torch.empty_like(kc) if kc is not None else None
     stream = torch.cuda.current_stream()
     kbuf, vbuf = inp["k_buf"], inp["v_buf"]
+    # In-place, per layer: layer l's selection and compaction only need its own
+    # scores and cache, so they run on a second stream (default priority, its
+    # own workspace) while layer l + 1 is scored; the step ends when both
+    # streams have drained.
+    overlap = per_layer and not args.serial_layers
+    side = torch.cuda.Stream() if overlap else stream
+    ws_side = torch.empty_like(ws) if overlap else ws
+    scored = [torch.cuda.Event() for _ in range(L)] if overlap else None
+    drained = torch.cuda.Event() if overlap else None
 
     def step():
         if not per_layer:
@@ -352,10 +364,16 @@ def bench_speckv(args, cfg, torch, skv, wl):
             for layer in range(L):
                 skv.speckv_scores(shape, inp["q_obs"][layer:layer + 1], kbuf[layer:layer + 1], scores[layer:layer + 1],
                                   ws, stream)
+                if overlap:
+                    scored[layer].record(stream)
+                    side.wait_event(scored[layer])
                 skv.speckv_select(shape, scores[layer:layer + 1], cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel,
-                                  kept[layer:layer + 1], pooled[layer:layer + 1], ws, stream)
+                                  kept[layer:layer + 1], pooled[layer:layer + 1], ws_side, side)
                 skv.speckv_compact(shape, kbuf[layer:layer + 1], vbuf[layer:layer + 1], kept[layer:layer + 1], n_keep,
-                                   kbuf[layer:layer + 1], vbuf[layer:layer + 1], ws, stream)
+                                   kbuf[layer:layer + 1], vbuf[layer:layer + 1], ws_side, side)
+            if overlap:
+                drained.record(side)
+                stream.wait_event(drained)
 
     print(f"[bench] inputs ready ({gen_s:.1f} s); warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -407,6 +425,7 @@ def bench_speckv(args, cfg, torch, skv, wl):
         "config": {"workload": cfg.name, "n_layers": L, "n_q_heads": cfg.n_q_heads, "n_kv_heads": Hkv, "head_dim": d,
                    "n_in": cfg.n_in, "n_window": cfg.n_window, "n_lookahead": cfg.n_lookahead, "C_max": cfg.C_max,
                    "pool_kernel": cfg.pool_kernel, "in_place": cfg.in_place, "keys_per_step": keys,
+                   **({"layer_overlap": overlap} if per_layer else {}),
                    "aggregation": args.aggregation, "per_query_head": bool(args.per_query_head)},
         "roofline": roof,
         "roofline_alu": roof_alu,
