@@ -538,12 +538,13 @@ static void plan_for(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan*
 }
 
 // Four key tiles per wave halve the LDS reads of the row operand per MFMA,
-// but coarsen the key split: they are taken only where the resident-key
-// registers allow them and every block still walks many key groups.  When
-// that needs fewer, longer blocks than the usual target (few units with long
-// keys), four tiles still win where the blocks make whole rounds over the
-// CUs (no tail): the row parts may then be cut one or two finer than the LDS
-// budget needs, and the plan with the fewest rounds is taken.
+// but coarsen the key split: they are taken where the resident-key
+// registers allow them and every block still walks at least 16 key groups at
+// the usual target.  Otherwise (few units, or few keys per unit) four tiles
+// still win where the blocks make whole rounds over the CUs, with no partly
+// filled last round, and every block walks at least 4 key groups: the row
+// parts may then be cut up to two finer than the LDS budget needs, and the
+// plan with the fewest rounds (the longest blocks) is taken.
 template <typename T, int D>
 static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan* pl) {
   plan_for<T, D, 2>(n_units, n_rows, n_keys, pl);
@@ -557,10 +558,10 @@ static void plan_pick(int64_t n_units, int64_t n_rows, int64_t n_keys, ScorePlan
     }
     int64_t best_rounds = 0;
     for (int64_t extra = 0; extra <= 2; ++extra) {
-      for (int64_t rounds = 1; rounds <= 4; ++rounds) {
+      for (int64_t rounds = 1; rounds <= 8; ++rounds) {
         plan_for<T, D, 4>(n_units, n_rows, n_keys, &p4, rounds * kCUs, extra);
         const int64_t blocks = n_units * p4.n_parts * p4.n_chunks;
-        if (p4.n_sub < 16 || blocks % kCUs != 0) continue;
+        if (p4.n_sub < 4 || blocks % kCUs != 0) continue;
         if (best_rounds == 0 || blocks / kCUs < best_rounds) {
           best_rounds = blocks / kCUs;
           *pl = p4;
