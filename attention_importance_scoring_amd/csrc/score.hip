@@ -22,8 +22,8 @@
 // MFMA operand, against every row tile of the part.  The main loop has no
 // barriers: the rows are read-only in LDS, each wave keeps its own row
 // statistics (pass 1) or column sums (pass 2), and the waves that share a
-// SIMD walk the row tiles in rotated orders, so that while one waits on its
-// MFMAs another runs its exp / sum work.  Pass 1 puts keys on
+// SIMD walk the row tiles half a sub-chunk apart, so that while one waits on
+// its MFMAs (or its next keys) another runs its exp / sum work.  Pass 1 puts keys on
 // the MFMA M dimension and rows on N, so each lane reduces one row in-lane;
 // pass 2 swaps the operands so that each lane owns one key column.  Every sum
 // has a fixed order (no floating-point atomics): results are run-to-run
@@ -153,16 +153,14 @@ __device__ __forceinline__ void load_keys(const ScoreArgs& a, int unit, int kbas
   }
 }
 
-// Iteration it of a wave: sub-chunk it / n_tiles, and row tile (it + rot) % n_tiles
-// of the staged part (the rotation staggers the two waves of a SIMD).
-struct IterPos {
-  int sc, j, rt;  // sub-chunk, position within the sub-chunk, row tile
-};
-__device__ __forceinline__ IterPos iter_pos(int it, int n_tiles, int rot) {
-  const int sc = it / n_tiles, j = it - sc * n_tiles;
-  int rt = j + rot;
-  rt -= (rt >= n_tiles) ? n_tiles : 0;
-  return {sc, j, rt};
+// A wave's walk over (sub-chunk, row tile) starts rot tiles into sub-chunk 0
+// and ends with sub-chunk 0's first rot tiles.  The waves that share a SIMD
+// (w, w + 4, ...) take rot = 0, n_tiles / 2 (or thirds at 12 waves): they
+// work on different row tiles at any time, and one reloads its keys at a
+// sub-chunk boundary while the other is mid-way through its sub-chunk.
+template <int WAVES>
+__device__ __forceinline__ int wave_phase(int wave, int n_tiles) {
+  return (wave / 4) * n_tiles / (WAVES / 4);
 }
 
 // Pass-1 key mask of one wave for one row: keys past `rel` (offset in the
@@ -285,32 +283,37 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     // pads with zero rows, whose statistics are never written), so the parts
     // of a chunk read each key group at the same pace and share it in L2.
     const int n_tiles = a.rows_per_part / 32;
-    const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
+    const int rot = wave_phase<Gm::kWaves>(wave, n_tiles);
     const int n_iter = n_sub * n_tiles;
     stage_rows<T, D, KT>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     __syncthreads();
 
     u32x4 kst[Gm::kKT][Gm::kNV];  // resident keys of the current sub-chunk
     load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(0), kst);
-    bool masked = false;
-    for (int it = 0; it < n_iter; ++it) {
-      const IterPos cu = iter_pos(it, n_tiles, rot);
-      if (cu.j == 0) {  // new sub-chunk
-        if (cu.sc > 0) load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(cu.sc), kst);
-        masked = sub_masked(cu.sc);
+    int sc = 0, rt = rot;  // current sub-chunk and row tile
+    bool masked = sub_masked(0);
+    for (int it = 0; it < n_iter; ++it, ++rt) {
+      if (rt == n_tiles) {  // next sub-chunk; after the last one, back to sub-chunk 0 for its first rot tiles
+        rt = 0;
+        const int nsc = sc + 1 == n_sub ? 0 : sc + 1;
+        if (nsc != sc) {
+          sc = nsc;
+          load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(sc), kst);
+          masked = sub_masked(sc);
+        }
       }
       u32x4 qf[Gm::kNV];
       if constexpr (Gm::kPrio) mfma_prio<1>();
-      read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
+      read_q_frag<T, D, KT>(s_q, rt, lane, qf);
       f32x16 acc[Gm::kKT];
-      const int r = cu.rt * 32 + lane % 32;
+      const int r = rt * 32 + lane % 32;
       if (masked)
-        pass1_mfma<T, D, KT, true>(kst, qf, pass1_rel(a, wave_kbase(cu.sc), row0 + r, half), acc);
+        pass1_mfma<T, D, KT, true>(kst, qf, pass1_rel(a, wave_kbase(sc), row0 + r, half), acc);
       else
         pass1_mfma<T, D, KT, false>(kst, qf, 0, acc);
       if constexpr (Gm::kPrio) mfma_prio<0>();
       RowStat st;
-      if (cu.sc == 0) {  // first visit of the row in this part: exact (max, sum)
+      if (it < n_tiles) {  // first visit of the row in this part: exact (max, sum)
         st = masked ? pass1_stats<T, D, KT, true>(acc, c) : pass1_stats<T, D, KT, false>(acc, c);
       } else {
         // Later visits sum against the row's reference (the maximum of its
@@ -453,7 +456,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     const int row0 = bp.part * a.rows_per_part;
     const int prow = min(a.rows_per_part, a.n_rows - row0);
     const int n_tiles = (prow + 31) / 32;
-    const int rot = (wave / 4) * n_tiles / (Gm::kWaves / 4);  // waves w, w + 4, ... share a SIMD
+    const int rot = wave_phase<Gm::kWaves>(wave, n_tiles);
     const int n_iter = n_sub * n_tiles;
     stage_rows<T, D, KT>(s_q, qrows + (int64_t)row0 * Gm::RF::kRowBytes, prow, n_tiles * 32);
     for (int r = threadIdx.x; r < n_tiles * 32; r += Gm::kThreads) s_lam[r] = (r < prow) ? lam_unit[row0 + r] : INFINITY;
@@ -464,16 +467,35 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
     float colsum[Gm::kKT];
 #pragma unroll
     for (int kt = 0; kt < Gm::kKT; ++kt) colsum[kt] = 0.f;
-    int in_sum = 0;  // tiles of the current sub-chunk done
-    for (int it = 0; it < n_iter; ++it) {
-      const IterPos cu = iter_pos(it, n_tiles, rot);
-      if (cu.j == 0 && cu.sc > 0) load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(cu.sc), kst);  // new sub-chunk
+    // Column sums of sub-chunk sc for this part: stored, or (the second
+    // stretch of sub-chunk 0, after the wrap) combined with the first one.
+    auto flush = [&](int sc, bool combine) {
+      const int kbase = wave_kbase(sc);
+#pragma unroll
+      for (int kt = 0; kt < Gm::kKT; ++kt) {
+        const float tot = agg2<MAX>(colsum[kt], shfl_xor32(colsum[kt]));
+        const int key = kbase + kt * 32 + lane;
+        if (lane < 32 && key < a.n_keys) out[key] = combine ? agg2<MAX>(out[key], tot) : tot;
+        colsum[kt] = 0.f;
+      }
+    };
+    int sc = 0, rt = rot;  // current sub-chunk and row tile
+    for (int it = 0; it < n_iter; ++it, ++rt) {
+      if (rt == n_tiles) {  // next sub-chunk; after the last one, back to sub-chunk 0 for its first rot tiles
+        rt = 0;
+        const int nsc = sc + 1 == n_sub ? 0 : sc + 1;
+        if (nsc != sc) {
+          flush(sc, false);
+          sc = nsc;
+          load_keys<T, D, KT, ROWS>(a, unit, wave_kbase(sc), kst);
+        }
+      }
       float lam[16];
-      read_lam(cu.rt, lam);
+      read_lam(rt, lam);
       f32x16 acc[Gm::kKT];
       u32x4 qf[Gm::kNV];
       if constexpr (Gm::kPrio) mfma_prio<1>();
-      read_q_frag<T, D, KT>(s_q, cu.rt, lane, qf);
+      read_q_frag<T, D, KT>(s_q, rt, lane, qf);
       pass2_mfma<T, D, KT>(kst, qf, acc);
       if constexpr (Gm::kPrio) mfma_prio<0>();
       // acc[kt][i] = <q_(row0 + 32 rt + acc_row(i, half)), k_(kbase + 32 kt + lane % 32)>
@@ -486,18 +508,8 @@ __global__ __launch_bounds__((ScoreGeom<T, D, KT>::kThreads), 1) void score_pass
         for (int i = 4; i < 16; ++i) s4[i & 3] = agg2<MAX>(s4[i & 3], fast_exp2(__builtin_fmaf(acc[kt][i], c, -lam[i])));
         colsum[kt] = agg2<MAX>(colsum[kt], agg2<MAX>(agg2<MAX>(s4[0], s4[1]), agg2<MAX>(s4[2], s4[3])));
       }
-      if (++in_sum == n_tiles) {  // sub-chunk complete for this part: write, then restart the sums
-        const int kbase = wave_kbase(cu.sc);
-#pragma unroll
-        for (int kt = 0; kt < Gm::kKT; ++kt) {
-          const float tot = agg2<MAX>(colsum[kt], shfl_xor32(colsum[kt]));
-          const int key = kbase + kt * 32 + lane;
-          if (lane < 32 && key < a.n_keys) out[key] = tot;
-          colsum[kt] = 0.f;
-        }
-        in_sum = 0;
-      }
     }
+    flush(sc, rot > 0 && n_sub > 1);
   }
 }
 
