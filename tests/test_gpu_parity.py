@@ -375,6 +375,15 @@ def test_specpc_small(case):
     _specpc_check(wl.reduced(wl.SPECPC_DRAFT_32K, **case), seed=21)
 
 
+@pytest.mark.parametrize("l_skip", [1, 2])
+def test_specpc_workspace_of_the_size_query_for_every_l_skip(l_skip):
+    # The workspace is exactly the size speckv_workspace_bytes returns for the
+    # shape (l_skip is not part of it): fewer used layers re-plan the passes
+    # with more key chunks, whose partials must still fit.
+    _specpc_check(wl.reduced(wl.SPECPC_DRAFT_32K, n_layers=3, n_q_heads=2, n_kv_heads=2, n_in=65536, window=1024,
+                             l_skip=l_skip, k_top=2048), seed=23)
+
+
 def test_specpc_user_weights_and_fp32():
     cfg = wl.reduced(wl.SPECPC_DRAFT_32K, n_layers=2, l_skip=1, n_in=640, window=70, k_top=50, dtype="f32")
     w = np.random.default_rng(0).random(70) + 0.05
