@@ -67,6 +67,16 @@ def test_tiny_fp32_2k_full():
     _full_check(wl.TINY_FP32_2K, seed=1)
 
 
+@pytest.mark.parametrize("case", [
+    dict(n_layers=2, n_in=30064),   # 16 units, 30000 keys: 4 row parts x 4 key chunks of 8 groups, ragged last group
+    dict(n_layers=1, n_in=65500),   # 8 units, 65436 keys: 4 row parts x 8 chunks, ragged last group
+], ids=["16-units-30000-keys", "8-units-65436-keys"])
+def test_few_long_units_whole_rounds_of_four_tile_blocks(case):
+    # Few units with long keys: the planner cuts the rows finer so that blocks of
+    # four key tiles make whole rounds over the CUs (256 blocks here).
+    _full_check(wl.reduced(wl.LLAMA8B_128K_INPLACE, C_max=1024, **case), seed=31)
+
+
 def test_fp32_d64_group_16():
     # fp32 at head_dim 64 with 16 query heads per KV head (1024 rows)
     cfg = wl.reduced(wl.TINY_FP32_2K, n_layers=2, n_q_heads=16, n_kv_heads=1, n_in=1300, n_window=24, n_lookahead=40,
