@@ -124,26 +124,16 @@ __device__ __forceinline__ void specpc_pass2_block(const SpecPCArgs& pa, int rb,
 #pragma unroll
     for (int r = 0; r < Gm::kRT; ++r) {
       // Keys after a row's position start at -inf (causal mask), so they add 0.
-      f32x16 sacc[Gm::kKT];
-      if constexpr (!MASKED) {
-#pragma unroll
-        for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = f32x16{};
-      } else {
+      int rel = 4096;
+      if constexpr (MASKED) {
         int64_t rel64 = a.pos_base + row0 + r * 32 + 4 * half - (kbase + (lane % 32));
         rel64 = rel64 < -4096 ? -4096 : (rel64 > 4096 ? 4096 : rel64);
-        const int rel = (int)rel64;
-#pragma unroll
-        for (int kt = 0; kt < Gm::kKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kt][i] = (kt * 32 - 8 * (i >> 2) - (i & 3) <= rel) ? 0.f : -INFINITY;
+        rel = (int)rel64;
       }
       const char* trow = rows + (r * 32 + lane % 32) * Gm::kRowPitch + half * Gm::RF::kHalfBytes;
+      u32x4 qv[Gm::kNV];
 #pragma unroll
-      for (int v = 0; v < Gm::kNV; ++v) {
-        const u32x4 qv = *reinterpret_cast<const u32x4*>(trow + v * 16);
-#pragma unroll
-        for (int kt = 0; kt < Gm::kKT; ++kt) sacc[kt] = Mfma<T>::step(qv, kst[kt][v], sacc[kt]);
-      }
+      for (int v = 0; v < Gm::kNV; ++v) qv[v] = *reinterpret_cast<const u32x4*>(trow + v * 16);
       float lam[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -153,11 +143,22 @@ __device__ __forceinline__ void specpc_pass2_block(const SpecPCArgs& pa, int rb,
         lam[4 * g4 + 2] = l4[2];
         lam[4 * g4 + 3] = l4[3];
       }
+      // One key tile at a time: its MFMAs, then its exp / add work.
 #pragma unroll
-      for (int kt = 0; kt < Gm::kKT; ++kt)
+      for (int kt = 0; kt < Gm::kKT; ++kt) {
+        f32x16 sacc;
+        if constexpr (!MASKED) {
+          sacc = f32x16{};
+        } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][kt][i] += fast_exp2(__builtin_fmaf(sacc[kt][i], c, -lam[i]));
-      __builtin_amdgcn_sched_barrier(0);  // keep the two row tiles' live ranges apart
+          for (int i = 0; i < 16; ++i) sacc[i] = (kt * 32 - 8 * (i >> 2) - (i & 3) <= rel) ? 0.f : -INFINITY;
+        }
+#pragma unroll
+        for (int v = 0; v < Gm::kNV; ++v) sacc = Mfma<T>::step(qv[v], kst[kt][v], sacc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][kt][i] += fast_exp2(__builtin_fmaf(sacc[i], c, -lam[i]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
