@@ -8,6 +8,9 @@ and resident in HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+Without --warmup, the untimed warm-up runs at least 3 steps and at least 0.3 s
+of them: from idle the GPU takes tens of milliseconds of sustained work to
+reach its steady clocks, longer than a few steps of the shorter workloads.
 --gpus N with N > 1 is refused: the path runs on one GPU.
 """
 from __future__ import annotations
@@ -45,7 +48,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 3, and at least 0.3 s of steps, so that the GPU's "
+                        "clocks have settled before the timed steps)")
     p.add_argument("--workload", default="qwen32b_shape_64k",
                    choices=["qwen32b_shape_64k", "llama8b_shape_16k", "llama8b_shape_128k_inplace", "specpc_draft_32k",
                             "speckv_pc_cascade_32k", "decode_qwen32b_shape_64k"])
@@ -254,6 +259,26 @@ def cascade_cpu_baseline(cc, inp):
                       f"prompt {kv_wall:.1f} s (wall)"}
 
 
+WARMUP_MIN_S = 0.3  # default warm-up: at least this long (and at least 3 steps)
+
+
+def warm_up(step, args, torch):
+    """The untimed warm-up: args.warmup steps when given; otherwise at least 3
+    steps and at least WARMUP_MIN_S seconds of them, each synchronized so that
+    host time follows GPU time.  Sets args.warmup to the number run."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return
+    n, t0 = 0, time.perf_counter()
+    while n < 3 or time.perf_counter() - t0 < WARMUP_MIN_S:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    args.warmup = n
+
+
 def timed_steps(step, steps, stream, torch):
     """Runs `steps` steps on `stream` between events: returns (mean ms over
     the bracketed region, per-step ms from an event after every step)."""
@@ -375,10 +400,8 @@ def bench_speckv(args, cfg, torch, skv, wl):
                 drained.record(side)
                 stream.wait_event(drained)
 
-    print(f"[bench] inputs ready ({gen_s:.1f} s); warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
+    print(f"[bench] inputs ready ({gen_s:.1f} s); warmed up over {args.warmup} steps", file=sys.stderr, flush=True)
     skv.profile_enable(True)
     ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
@@ -458,9 +481,7 @@ def bench_specpc(args, cfg, torch, skv, wl):
         skv.specpc_token_scores(shape, cfg.l_skip, inp["q_win"], inp["k"], None, ts, ws, stream)
         skv.speckv_select(sel, ts, cfg.k_top, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws, stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
     skv.profile_enable(True)
     ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
@@ -546,9 +567,7 @@ def bench_cascade(args, cc, torch, skv, wl):
                               stream)
             skv.speckv_compact(s2_shape, k_tok, v_tok, kept, n_keep, kc, vc, ws2, stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
     skv.profile_enable(True)
     ms, per_step = timed_steps(step, args.steps, stream, torch)
     prof = skv.profile_read()
@@ -609,9 +628,7 @@ def bench_decode(args, cfg, torch, skv, wl):
     def timed(sh, n_rows, k, v, reps):
         n_ws = skv.speckv_decode_workspace_bytes(sh, n_rows)
         w = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws else None
-        for _ in range(args.warmup):
-            skv.speckv_decode_attention(sh, n_rows, q, k, v, out, w, stream)
-        torch.cuda.synchronize()
+        warm_up(lambda: skv.speckv_decode_attention(sh, n_rows, q, k, v, out, w, stream), args, torch)
         skv.profile_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
