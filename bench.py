@@ -71,8 +71,8 @@ def parse():
     p.add_argument("--cascade-path", choices=["rows", "gather"], default="rows",
                    help="cascade: SpecKV through the kept-token list, or on a gathered copy of the target cache")
     p.add_argument("--serial-layers", action="store_true",
-                   help="in-place workload: run each layer's selection and compaction on the scoring stream, "
-                        "after its scores (default: on a second stream, beside the next layer's scoring)")
+                   help="in-place workload: every layer's calls on one stream (default: the layers alternate "
+                        "between two streams, so that one layer's work overlaps the next one's)")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -370,15 +370,15 @@ def bench_speckv(args, cfg, torch, skv, wl):
     vc = torch.empty_like(kc) if kc is not None else None
     stream = torch.cuda.current_stream()
     kbuf, vbuf = inp["k_buf"], inp["v_buf"]
-    # In-place, per layer: layer l's selection and compaction only need its own
-    # scores and cache, so they run on a second stream (default priority, its
-    # own workspace) while layer l + 1 is scored; the step ends when both
-    # streams have drained.
+    # In place, one layer per call: the layers share nothing, so they alternate
+    # between two streams (default priority, a workspace each); layer l's
+    # selection and compaction and the block rounds of its passes overlap
+    # layer l + 1's work.  The second stream starts each step after the first
+    # one's previous step, and the step ends when both have drained.
     overlap = per_layer and not args.serial_layers
-    side = torch.cuda.Stream() if overlap else stream
-    ws_side = torch.empty_like(ws) if overlap else ws
-    scored = [torch.cuda.Event() for _ in range(L)] if overlap else None
-    drained = torch.cuda.Event() if overlap else None
+    streams = [stream, torch.cuda.Stream()] if overlap else [stream]
+    wss = [ws, torch.empty_like(ws)] if overlap else [ws]
+    begun, drained = (torch.cuda.Event(), torch.cuda.Event()) if overlap else (None, None)
 
     def step():
         if not per_layer:
@@ -386,18 +386,17 @@ def bench_speckv(args, cfg, torch, skv, wl):
             skv.speckv_select(shape, scores, cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept, pooled, ws, stream)
             skv.speckv_compact(shape, kbuf, vbuf, kept, n_keep, kc, vc, ws, stream)
         else:
-            for layer in range(L):
-                skv.speckv_scores(shape, inp["q_obs"][layer:layer + 1], kbuf[layer:layer + 1], scores[layer:layer + 1],
-                                  ws, stream)
-                if overlap:
-                    scored[layer].record(stream)
-                    side.wait_event(scored[layer])
-                skv.speckv_select(shape, scores[layer:layer + 1], cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel,
-                                  kept[layer:layer + 1], pooled[layer:layer + 1], ws_side, side)
-                skv.speckv_compact(shape, kbuf[layer:layer + 1], vbuf[layer:layer + 1], kept[layer:layer + 1], n_keep,
-                                   kbuf[layer:layer + 1], vbuf[layer:layer + 1], ws_side, side)
             if overlap:
-                drained.record(side)
+                begun.record(stream)
+                streams[1].wait_event(begun)
+            for layer in range(L):
+                st, w, sl = streams[layer % len(streams)], wss[layer % len(wss)], slice(layer, layer + 1)
+                skv.speckv_scores(shape, inp["q_obs"][sl], kbuf[sl], scores[sl], w, st)
+                skv.speckv_select(shape, scores[sl], cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept[sl],
+                                  pooled[sl], w, st)
+                skv.speckv_compact(shape, kbuf[sl], vbuf[sl], kept[sl], n_keep, kbuf[sl], vbuf[sl], w, st)
+            if overlap:
+                drained.record(streams[1])
                 stream.wait_event(drained)
 
     warm_up(step, args, torch)

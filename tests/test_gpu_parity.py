@@ -289,37 +289,36 @@ def test_in_place_equals_out_of_place_and_deterministic():
     assert_compacted(c["k_c"], c["v_c"], k0, v0, c["kept"])
 
 
-def test_in_place_layers_with_selection_on_a_second_stream():
-    """Per-layer in-place calls with each layer's selection and compaction on a
-    second stream (own workspace) beside the next layer's scoring, as bench.py
-    runs the 128K in-place workload: identical to one stream, bit for bit."""
+def test_in_place_layers_alternating_between_two_streams():
+    """Per-layer in-place calls with the layers alternating between two
+    streams (a workspace each), as bench.py runs the 128K in-place workload:
+    identical to one stream, bit for bit."""
     cfg = wl.reduced(wl.LLAMA8B_128K_INPLACE, n_layers=6, n_in=20000, n_window=64, n_lookahead=64, C_max=1000)
-    print(f"\n[case] {cfg.name} reduced: 6 layers one per call, n_in=20000, selection on a second stream", flush=True)
+    print(f"\n[case] {cfg.name} reduced: 6 layers one per call, n_in=20000, layers on two streams", flush=True)
     host = wl.speckv_inputs(cfg, 11, "cpu")
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     results = []
-    for overlap in (False, True):
+    for n_streams in (1, 2):
         inp = _to(host, "cuda")
         shape = shape_of(cfg, kv_head_stride=inp["kv_head_stride"], n_layers=1)
-        ws = workspace(shape, cfg.C_max)
         main = torch.cuda.current_stream()
-        side = torch.cuda.Stream() if overlap else main
-        ws_side = workspace(shape, cfg.C_max) if overlap else ws
+        streams = [main] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+        wss = [workspace(shape, cfg.C_max) for _ in range(n_streams)]
         n_keep = skv.speckv_n_keep(shape, cfg.C_max)
         scores = torch.full((L, H, cfg.n_pre), float("nan"), dtype=torch.float32, device="cuda")
         pooled = torch.full_like(scores, float("nan"))
         kept = torch.full((L, H, n_keep), -1, dtype=torch.int32, device="cuda")
+        begun = torch.cuda.Event()
+        begun.record(main)
+        for st in streams[1:]:
+            st.wait_event(begun)
         for i in range(L):
-            sl = slice(i, i + 1)
-            skv.speckv_scores(shape, inp["q_obs"][sl], inp["k_buf"][sl], scores[sl], ws, main)
-            if overlap:
-                ev = torch.cuda.Event()
-                ev.record(main)
-                side.wait_event(ev)
+            sl, st, w = slice(i, i + 1), streams[i % n_streams], wss[i % n_streams]
+            skv.speckv_scores(shape, inp["q_obs"][sl], inp["k_buf"][sl], scores[sl], w, st)
             skv.speckv_select(shape, scores[sl], cfg.C_max, skv.SKV_POOL_MAX, cfg.pool_kernel, kept[sl], pooled[sl],
-                              ws_side, side)
+                              w, st)
             skv.speckv_compact(shape, inp["k_buf"][sl], inp["v_buf"][sl], kept[sl], n_keep, inp["k_buf"][sl],
-                               inp["v_buf"][sl], ws_side, side)
+                               inp["v_buf"][sl], w, st)
         torch.cuda.synchronize()
         results.append((scores.cpu(), kept.cpu(), inp["k_buf"][:, :, :n_keep * d].cpu(),
                         inp["v_buf"][:, :, :n_keep * d].cpu()))
