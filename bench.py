@@ -419,7 +419,11 @@ def bench_speckv(args, cfg, torch, skv, wl):
     avg_s = kern[dom]["avg_ms"] * 1e-3
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = flops_per_launch / avg_s / 1e12
-    roof = {"kernel": dom, "scope": "one launch of the dominant kernel (not the whole step; see path_mfma)",
+    scope = "one launch of the dominant kernel (not the whole step; see path_mfma)"
+    if overlap:
+        scope += ("; the layers alternate between two streams, so a launch's event-timed duration includes the other "
+                  "stream's overlapping work and achieved is a lower bound (--serial-layers times launches alone)")
+    roof = {"kernel": dom, "scope": scope,
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, cfg.name, f"speckv_kernels_{cfg.name}_traffic.json") if default_variant else None}
     # whole path against the MFMA roofline: one Q_obs K^T is the method's algorithmic work
