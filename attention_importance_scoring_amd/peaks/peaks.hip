@@ -143,9 +143,11 @@ __global__ __launch_bounds__(1024) void valu_kernel(int iters, float seed, float
 // MODE 1: the MFMAs alone (one add per tile keeps them live); MODE 2: the
 // vector work alone (on values the compiler cannot precompute).  PRIO raises
 // the issue priority around the MFMAs, as the scoring kernels do at two waves
-// per SIMD.  The empty asm statements mark the row operand as changed every
-// step, so that nothing is hoisted out of the loop; they emit no instruction.
-template <int KT, int NV, int MODE, bool PRIO, int WAVES>
+// per SIMD.  KTMAJ orders a step key tile by key tile (the NV MFMAs of one
+// tile, then its vector work) instead of all MFMAs first.  The empty asm
+// statements mark the row operand as changed every step, so that nothing is
+// hoisted out of the loop; they emit no instruction.
+template <int KT, int NV, int MODE, bool PRIO, int WAVES, bool KTMAJ = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void mix_kernel(int iters, float seed, float* sink,
                                                              unsigned long long* clk) {
   typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -166,6 +168,25 @@ __global__ __launch_bounds__(WAVES * 64, 1) void mix_kernel(int iters, float see
 #pragma unroll
     for (int i = 0; i < 16; ++i) vals[kt][i] = (float)(i + kt) * seed;
   for (int it = 0; it < iters; ++it) {
+    if constexpr (KTMAJ) {
+      static_assert(MODE == 0, "key-tile order is a form of the mix");
+#pragma unroll
+      for (int v = 0; v < NV; ++v) asm volatile("" : "+v"(b[v]));
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kt][v]),
+                                                        __builtin_bit_cast(bf16x8, b[v]), acc, 0, 0, 0);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], c, -ref));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      continue;
+    }
     f32x16 acc[KT];
     if constexpr (MODE == 2) {
 #pragma unroll
@@ -308,6 +329,7 @@ int main(int argc, char** argv) {
       {"d128_mix_2w_prio", 4, 8, {}, 0},        {"d128_mix_3w_kt2", 2, 12, {}, 0},
       {"d128_mix_3w_kt2_prio", 2, 12, {}, 0},   {"d64_mfma_only_3w", 4, 12, {}, 0},
       {"d64_mix_3w", 4, 12, {}, 0},             {"d64_mix_2w_prio", 4, 8, {}, 0},
+      {"d128_mix_2w_prio_ktmajor", 4, 8, {}, 0},
   };
   for (Mix& m : mixes) m.iters = tiles / m.kt;
   const float c = 0.1275f;
@@ -321,6 +343,8 @@ int main(int argc, char** argv) {
   mixes[7].r = time_best([&] { mix_kernel<4, 4, 1, false, 12><<<cus, 768>>>(mixes[7].iters, c, fsink, d_clk); }, d_clk);
   mixes[8].r = time_best([&] { mix_kernel<4, 4, 0, false, 12><<<cus, 768>>>(mixes[8].iters, c, fsink, d_clk); }, d_clk);
   mixes[9].r = time_best([&] { mix_kernel<4, 4, 0, true, 8><<<cus, 512>>>(mixes[9].iters, c, fsink, d_clk); }, d_clk);
+  mixes[10].r = time_best([&] { mix_kernel<4, 8, 0, true, 8, true><<<cus, 512>>>(mixes[10].iters, c, fsink, d_clk); },
+                          d_clk);
   CK(hipDeviceSynchronize());
 
   std::printf("device %s, %d CUs, wall clock %d kHz\n", prop.gcnArchName, cus, wall_khz);
