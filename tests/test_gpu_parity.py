@@ -77,6 +77,17 @@ def test_few_long_units_whole_rounds_of_four_tile_blocks(case):
     _full_check(wl.reduced(wl.LLAMA8B_128K_INPLACE, C_max=1024, **case), seed=31)
 
 
+@pytest.mark.parametrize("case", [
+    (wl.TINY_FP32_2K, dict(n_layers=2, n_q_heads=64, n_kv_heads=8, n_in=30032, n_window=32, n_lookahead=32,
+                           C_max=500)),   # fp32: 16 units of 512 rows, 2 parts x 8 chunks of 4 groups
+    (wl.LLAMA8B_16K, dict(n_layers=4, head_dim=64, n_in=20016, n_window=16, n_lookahead=64, C_max=800)),
+    # bf16: 32 units of 320 rows, 2 parts x 4 chunks of 4 groups
+], ids=["fp32-d64-16-units", "bf16-d64-32-units"])
+def test_whole_rounds_of_four_tile_blocks_at_head_dim_64(case):
+    base, changes = case
+    _full_check(wl.reduced(base, **changes), seed=37)
+
+
 def test_fp32_d64_group_16():
     # fp32 at head_dim 64 with 16 query heads per KV head (1024 rows)
     cfg = wl.reduced(wl.TINY_FP32_2K, n_layers=2, n_q_heads=16, n_kv_heads=1, n_in=1300, n_window=24, n_lookahead=40,
