@@ -223,6 +223,89 @@ __global__ __launch_bounds__(WAVES * 64, 1) void mix_kernel(int iters, float see
   clock_mark(clk, 1);
 }
 
+// The pass-2 tile with its LDS traffic: per step a wave reads its row operand
+// (32 rows x 256 bytes, padded pitch) and its 16 rows' lse values from LDS, as
+// score_pass2_kernel does, then for 4 key tiles forms the 32 x 32 scores with
+// 8 MFMAs each and adds 2^(c s - lse) per element into a column sum.  KTMAJ
+// as in mix_kernel.  Two waves per SIMD with the MFMA issue priority.
+template <bool KTMAJ>
+__global__ __launch_bounds__(8 * 64, 1) void mix_lds_kernel(int iters, float seed, float* sink,
+                                                           unsigned long long* clk) {
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  constexpr int KT = 4, kTiles = 12, kPitch = 272;
+  __shared__ __attribute__((aligned(16))) char s_q[kTiles * 32 * kPitch];
+  __shared__ __attribute__((aligned(16))) float s_lam[kTiles * 32];
+  for (int i = threadIdx.x; i < kTiles * 32 * kPitch / 16; i += 8 * 64)
+    reinterpret_cast<u32x4*>(s_q)[i] = u32x4{0x3f803f80u ^ (unsigned)i, 0x3e003f00u, 0xbf00be80u, 0x3c003c00u};
+  for (int i = threadIdx.x; i < kTiles * 32; i += 8 * 64) s_lam[i] = 2.0f + 0.001f * (float)i;
+  __syncthreads();
+  clock_mark(clk, 0);
+  const unsigned lane = threadIdx.x % 64, wave = threadIdx.x / 64, half = lane / 32;
+  u32x4 a[KT][8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) a[kt][v] = u32x4{0x3f00bf00u + lane, 0x3e80be80u ^ kt, 0x3d003d80u, 0x3f803f00u + v};
+  const float c = seed;
+  float col[KT] = {0.f, 0.f, 0.f, 0.f};
+  int rt = (wave / 4) * kTiles / 2;  // the two waves of a SIMD read different row tiles
+  for (int it = 0; it < iters; ++it) {
+    const char* p = s_q + (rt * 32 + lane % 32) * kPitch + half * 128;
+    const float* lrow = s_lam + rt * 32;
+    rt = rt + 1 == kTiles ? 0 : rt + 1;
+    float lam[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lrow[8 * g4 + 4 * half]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lam[4 * g4 + e] = l4[e];
+    }
+    u32x4 b[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) b[v] = *reinterpret_cast<const u32x4*>(p + v * 16);
+    if constexpr (KTMAJ) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_setprio(1);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[v]),
+                                                        __builtin_bit_cast(bf16x8, a[kt][v]), acc, 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], c, -lam[i]));
+        col[kt] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 acc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[v]),
+                                                            __builtin_bit_cast(bf16x8, a[kt][v]), acc[kt], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[kt][i], c, -lam[i]));
+        col[kt] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      }
+    }
+  }
+  const float t = (col[0] + col[1]) + (col[2] + col[3]);
+  if (t == 1234.5f) sink[0] = t;
+  clock_mark(clk, 1);
+}
+
 struct Result {
   float ms;
   double ghz;
@@ -329,7 +412,8 @@ int main(int argc, char** argv) {
       {"d128_mix_2w_prio", 4, 8, {}, 0},        {"d128_mix_3w_kt2", 2, 12, {}, 0},
       {"d128_mix_3w_kt2_prio", 2, 12, {}, 0},   {"d64_mfma_only_3w", 4, 12, {}, 0},
       {"d64_mix_3w", 4, 12, {}, 0},             {"d64_mix_2w_prio", 4, 8, {}, 0},
-      {"d128_mix_2w_prio_ktmajor", 4, 8, {}, 0},
+      {"d128_mix_2w_prio_ktmajor", 4, 8, {}, 0}, {"d128_lds_mix_2w_prio", 4, 8, {}, 0},
+      {"d128_lds_mix_2w_prio_ktmajor", 4, 8, {}, 0},
   };
   for (Mix& m : mixes) m.iters = tiles / m.kt;
   const float c = 0.1275f;
@@ -345,6 +429,8 @@ int main(int argc, char** argv) {
   mixes[9].r = time_best([&] { mix_kernel<4, 4, 0, true, 8><<<cus, 512>>>(mixes[9].iters, c, fsink, d_clk); }, d_clk);
   mixes[10].r = time_best([&] { mix_kernel<4, 8, 0, true, 8, true><<<cus, 512>>>(mixes[10].iters, c, fsink, d_clk); },
                           d_clk);
+  mixes[11].r = time_best([&] { mix_lds_kernel<false><<<cus, 512>>>(mixes[11].iters, c, fsink, d_clk); }, d_clk);
+  mixes[12].r = time_best([&] { mix_lds_kernel<true><<<cus, 512>>>(mixes[12].iters, c, fsink, d_clk); }, d_clk);
   CK(hipDeviceSynchronize());
 
   std::printf("device %s, %d CUs, wall clock %d kHz\n", prop.gcnArchName, cus, wall_khz);
